@@ -1,0 +1,477 @@
+// C ABI front end: argument validation (all of it before any side effect),
+// the host FIFO block pool, the new block tables and lengths, workspace
+// layout, and the stream-ordered launch sequence score -> select -> compact.
+
+#include "../../include/kara.h"
+#include "kara_internal.hpp"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <deque>
+#include <string>
+#include <vector>
+
+struct kara_pool {
+  int32_t n_blocks;
+  std::deque<int32_t> fifo;
+  std::vector<uint8_t> is_free;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+kara_status fail(kara_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+kara_status hip_fail(hipError_t e, const char* what) {
+  return fail(KARA_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+kara_status check_shape(const kara_shape* sh) {
+  if (!sh) return fail(KARA_E_INVAL, "shape is NULL");
+  if (sh->n_layers < 1 || sh->n_q_heads < 1 || sh->n_kv_heads < 1 || sh->block_size < 1)
+    return fail(KARA_E_INVAL, "shape: layers, heads and block size must be >= 1");
+  if (sh->n_q_heads % sh->n_kv_heads != 0)
+    return fail(KARA_E_INVAL, "shape: n_q_heads (%d) is not a multiple of n_kv_heads (%d)",
+                sh->n_q_heads, sh->n_kv_heads);
+  if (sh->dtype != KARA_F32 && sh->dtype != KARA_BF16)
+    return fail(KARA_E_UNSUPPORTED, "shape: dtype %d not supported", sh->dtype);
+  if (sh->head_dim != 64 && sh->head_dim != 128)
+    return fail(KARA_E_UNSUPPORTED, "shape: head_dim %d not supported (64 or 128)", sh->head_dim);
+  return KARA_OK;
+}
+
+kara_status check_params(const kara_params* p) {
+  if (!p) return fail(KARA_E_INVAL, "params is NULL");
+  if (p->window < 1 || p->window > kara::kMaxWindow)
+    return fail(KARA_E_INVAL, "window %d outside [1, %d]", p->window, kara::kMaxWindow);
+  if (p->protect < 0 || p->protect >= p->window)
+    return fail(KARA_E_INVAL, "protect %d outside [0, window)", p->protect);
+  const int C = p->window - p->protect;
+  if (C > kara::kMaxRegion)
+    return fail(KARA_E_INVAL, "compressible region %d exceeds %d", C, kara::kMaxRegion);
+  if (p->top_k < 1 || p->top_k > C) return fail(KARA_E_INVAL, "top_k %d outside [1, %d]", p->top_k, C);
+  if (p->budget < 1 || p->budget > C) return fail(KARA_E_INVAL, "budget %d outside [1, %d]", p->budget, C);
+  return KARA_OK;
+}
+
+size_t elt_size(const kara_shape* sh) { return sh->dtype == KARA_BF16 ? 2 : 4; }
+
+// Sequence-level checks shared by every entry point that reads the pool.
+kara_status check_sequences(const kara_shape* sh, const kara_params* p, int32_t n_seqs,
+                            int32_t n_blocks, const int32_t* table_h, int32_t max_blocks,
+                            const int32_t* lens_h, const kara_pool* pool) {
+  if (n_seqs < 0) return fail(KARA_E_INVAL, "n_seqs < 0");
+  if (n_seqs == 0) return KARA_OK;
+  if (!table_h || !lens_h) return fail(KARA_E_INVAL, "host block table or lengths NULL");
+  if (n_blocks < 1 || max_blocks < 1) return fail(KARA_E_INVAL, "n_blocks and max_blocks must be >= 1");
+  const int bs = sh->block_size;
+  std::vector<uint8_t> seen((size_t)n_blocks, 0);
+  for (int32_t b = 0; b < n_seqs; ++b) {
+    const int64_t L = lens_h[b];
+    if (L < p->window) return fail(KARA_E_INVAL, "sequence %d: length %lld < window %d", b, (long long)L, p->window);
+    if (ceil_div(L, bs) > max_blocks)
+      return fail(KARA_E_INVAL, "sequence %d: length %lld needs more than max_blocks=%d blocks", b,
+                  (long long)L, max_blocks);
+    const int64_t f0 = (L - p->window) / bs;
+    const int64_t f1 = ceil_div(L, bs);
+    if (f0 + ceil_div((L - p->window) % bs + p->budget + p->protect, bs) > max_blocks)
+      return fail(KARA_E_INVAL, "sequence %d: compacted tail does not fit max_blocks", b);
+    for (int64_t e = f0; e < f1; ++e) {
+      const int32_t id = table_h[(size_t)b * max_blocks + e];
+      if (id < 0 || id >= n_blocks)
+        return fail(KARA_E_INVAL, "sequence %d: block table entry %lld = %d out of range [0, %d)", b,
+                    (long long)e, id, n_blocks);
+      if (seen[id]) return fail(KARA_E_INVAL, "block %d appears twice in the compressed tails", id);
+      seen[id] = 1;
+      if (pool && pool->n_blocks == n_blocks && pool->is_free[id])
+        return fail(KARA_E_INVAL, "block %d is in use by sequence %d but also free in the pool", id, b);
+    }
+  }
+  return KARA_OK;
+}
+
+struct Plan {
+  std::vector<int32_t> fresh;   // all fresh ids, sequences in call order
+  std::vector<int32_t> freed;   // old tail ids, sequences in call order, positions ascending
+};
+
+// Fills the new tables and lengths from the front of the pool without popping.
+kara_status make_plan(const kara_shape* sh, const kara_params* p, int32_t n_seqs,
+                      const int32_t* table_h, int32_t max_blocks, const int32_t* lens_h,
+                      const kara_pool* pool, int32_t* new_table_h, int32_t* new_lens_h, Plan* plan) {
+  const int bs = sh->block_size;
+  int64_t need = 0;
+  for (int32_t b = 0; b < n_seqs; ++b) {
+    const int64_t L = lens_h[b];
+    need += ceil_div((L - p->window) % bs + p->budget + p->protect, bs);
+  }
+  if (need > (int64_t)pool->fifo.size())
+    return fail(KARA_E_NOBLOCKS, "need %lld fresh blocks, pool has %zu", (long long)need, pool->fifo.size());
+  if (!new_table_h || !new_lens_h) return fail(KARA_E_INVAL, "host outputs NULL");
+  plan->fresh.assign(pool->fifo.begin(), pool->fifo.begin() + need);
+  plan->freed.clear();
+  size_t cur = 0;
+  for (int32_t b = 0; b < n_seqs; ++b) {
+    const int64_t L = lens_h[b];
+    const int64_t f0 = (L - p->window) / bs;
+    const int64_t n_new = ceil_div((L - p->window) % bs + p->budget + p->protect, bs);
+    const int32_t* row = table_h + (size_t)b * max_blocks;
+    int32_t* out = new_table_h + (size_t)b * max_blocks;
+    for (int64_t e = 0; e < f0; ++e) out[e] = row[e];
+    for (int64_t e = 0; e < n_new; ++e) out[f0 + e] = plan->fresh[cur++];
+    for (int64_t e = f0 + n_new; e < max_blocks; ++e) out[e] = -1;
+    new_lens_h[b] = (int32_t)(L - (p->window - p->protect) + p->budget);
+  }
+  for (int32_t b = 0; b < n_seqs; ++b) {
+    const int64_t L = lens_h[b];
+    const int64_t f0 = (L - p->window) / bs;
+    for (int64_t e = f0; e < ceil_div(L, bs); ++e) plan->freed.push_back(table_h[(size_t)b * max_blocks + e]);
+  }
+  return KARA_OK;
+}
+
+void commit_plan(kara_pool* pool, const Plan& plan) {
+  for (size_t i = 0; i < plan.fresh.size(); ++i) {
+    pool->is_free[pool->fifo.front()] = 0;
+    pool->fifo.pop_front();
+  }
+  for (int32_t id : plan.freed) {
+    pool->fifo.push_back(id);
+    pool->is_free[id] = 1;
+  }
+}
+
+// Workspace: [partial column sums of every 512-row chunk][retained positions]
+struct Workspace {
+  size_t partials, retained, total;
+};
+
+Workspace layout(const kara_shape* sh, const kara_params* p, int32_t n_seqs) {
+  const size_t U = (size_t)n_seqs * sh->n_layers * sh->n_kv_heads;
+  const int C = p->window - p->protect;
+  const int G = sh->n_q_heads / sh->n_kv_heads;
+  const size_t n_split = (size_t)kara::score_chunks(G, p->window);
+  Workspace w;
+  w.partials = 0;
+  w.retained = align_up(U * n_split * C * sizeof(float));
+  w.total = w.retained + align_up(U * p->budget * sizeof(int32_t));
+  return w;
+}
+
+kara::ScoreArgs score_args(const kara_shape* sh, const kara_params* p, int32_t n_seqs,
+                           const void* q, const void* kv, int32_t n_blocks, const int32_t* table_d,
+                           int32_t max_blocks, const int32_t* lens_d, float* out) {
+  kara::ScoreArgs a;
+  a.q = q;
+  a.pool = kv;
+  a.table = table_d;
+  a.lens = lens_d;
+  a.out = out;
+  a.S = n_seqs;
+  a.Lyr = sh->n_layers;
+  a.Hq = sh->n_q_heads;
+  a.Hkv = sh->n_kv_heads;
+  a.G = sh->n_q_heads / sh->n_kv_heads;
+  a.D = sh->head_dim;
+  a.bs = sh->block_size;
+  a.NB = n_blocks;
+  a.MB = max_blocks;
+  a.W = p->window;
+  a.C = p->window - p->protect;
+  a.n_split = kara::score_chunks(a.G, a.W);
+  a.n_units = n_seqs * sh->n_layers * sh->n_kv_heads;
+  a.c = (float)(1.4426950408889634 / std::sqrt((double)sh->head_dim));
+  return a;
+}
+
+kara::CompactArgs compact_args(const kara_shape* sh, const kara_params* p, int32_t n_seqs,
+                               void* kv, int32_t n_blocks, const int32_t* old_d, const int32_t* new_d,
+                               int32_t max_blocks, const int32_t* lens_d, const int32_t* retained_d) {
+  kara::CompactArgs a;
+  a.pool = kv;
+  a.old_table = old_d;
+  a.new_table = new_d;
+  a.lens = lens_d;
+  a.retained = retained_d;
+  a.S = n_seqs;
+  a.Lyr = sh->n_layers;
+  a.Hkv = sh->n_kv_heads;
+  a.row_bytes = (int)(sh->head_dim * elt_size(sh));
+  a.bs = sh->block_size;
+  a.NB = n_blocks;
+  a.MB = max_blocks;
+  a.W = p->window;
+  a.B = p->protect;
+  a.R = p->budget;
+  return a;
+}
+
+bool is_aligned(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* kara_last_error(void) { return g_err.c_str(); }
+
+const char* kara_version(void) { return "kara-mi355x 0.1 (gfx950)"; }
+
+kara_status kara_pool_create(int32_t n_blocks, const int32_t* free_ids, int32_t n_free, kara_pool** out) {
+  if (!out) return fail(KARA_E_INVAL, "out is NULL");
+  if (n_blocks < 1) return fail(KARA_E_INVAL, "n_blocks must be >= 1");
+  if (n_free < 0 || n_free > n_blocks || (n_free > 0 && !free_ids))
+    return fail(KARA_E_INVAL, "bad free list");
+  std::vector<uint8_t> is_free((size_t)n_blocks, 0);
+  for (int32_t i = 0; i < n_free; ++i) {
+    const int32_t id = free_ids[i];
+    if (id < 0 || id >= n_blocks) return fail(KARA_E_INVAL, "free id %d out of range", id);
+    if (is_free[id]) return fail(KARA_E_INVAL, "free id %d repeated", id);
+    is_free[id] = 1;
+  }
+  kara_pool* pl = new (std::nothrow) kara_pool;
+  if (!pl) return fail(KARA_E_INVAL, "out of host memory");
+  pl->n_blocks = n_blocks;
+  pl->fifo.assign(free_ids, free_ids + n_free);
+  pl->is_free.swap(is_free);
+  *out = pl;
+  return KARA_OK;
+}
+
+kara_status kara_pool_alloc(kara_pool* pool, int32_t n, int32_t* ids_out) {
+  if (!pool || n < 0 || (n > 0 && !ids_out)) return fail(KARA_E_INVAL, "bad arguments");
+  if ((size_t)n > pool->fifo.size())
+    return fail(KARA_E_NOBLOCKS, "need %d blocks, pool has %zu", n, pool->fifo.size());
+  for (int32_t i = 0; i < n; ++i) {
+    ids_out[i] = pool->fifo.front();
+    pool->is_free[ids_out[i]] = 0;
+    pool->fifo.pop_front();
+  }
+  return KARA_OK;
+}
+
+kara_status kara_pool_free(kara_pool* pool, const int32_t* ids, int32_t n) {
+  if (!pool || n < 0 || (n > 0 && !ids)) return fail(KARA_E_INVAL, "bad arguments");
+  std::vector<int32_t> seen;
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t id = ids[i];
+    if (id < 0 || id >= pool->n_blocks) return fail(KARA_E_INVAL, "id %d out of range", id);
+    if (pool->is_free[id]) return fail(KARA_E_INVAL, "id %d is already free", id);
+    for (int32_t x : seen)
+      if (x == id) return fail(KARA_E_INVAL, "id %d repeated", id);
+    seen.push_back(id);
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    pool->fifo.push_back(ids[i]);
+    pool->is_free[ids[i]] = 1;
+  }
+  return KARA_OK;
+}
+
+int32_t kara_pool_num_free(const kara_pool* pool) { return pool ? (int32_t)pool->fifo.size() : 0; }
+
+int32_t kara_pool_snapshot(const kara_pool* pool, int32_t* ids_out, int32_t cap) {
+  if (!pool || !ids_out || cap <= 0) return 0;
+  int32_t n = 0;
+  for (int32_t id : pool->fifo) {
+    if (n >= cap) break;
+    ids_out[n++] = id;
+  }
+  return n;
+}
+
+void kara_pool_destroy(kara_pool* pool) { delete pool; }
+
+size_t kara_workspace_bytes(const kara_shape* shape, const kara_params* params, int32_t n_seqs) {
+  if (check_shape(shape) != KARA_OK || check_params(params) != KARA_OK || n_seqs < 0) return 0;
+  return layout(shape, params, n_seqs).total;
+}
+
+kara_status kara_compress(const kara_shape* shape, const kara_params* params, int32_t n_seqs,
+                          const void* q_window, void* kv_pool, int32_t n_blocks,
+                          const int32_t* block_table_h, const int32_t* block_table_d,
+                          int32_t max_blocks, const int32_t* seq_lens_h, const int32_t* seq_lens_d,
+                          kara_pool* pool, int32_t* new_block_table_h, int32_t* new_block_table_d,
+                          int32_t* new_seq_lens_h, void* workspace, size_t workspace_bytes,
+                          void* stream, float* scores_out_d, int32_t* cand_out_d,
+                          int32_t* retained_out_d) {
+  kara_status st;
+  if ((st = check_shape(shape)) != KARA_OK) return st;
+  if ((st = check_params(params)) != KARA_OK) return st;
+  if (!pool) return fail(KARA_E_INVAL, "pool is NULL");
+  if (pool->n_blocks != n_blocks) return fail(KARA_E_INVAL, "pool covers %d blocks, cache has %d", pool->n_blocks, n_blocks);
+  if ((st = check_sequences(shape, params, n_seqs, n_blocks, block_table_h, max_blocks, seq_lens_h, pool)) != KARA_OK)
+    return st;
+  if (n_seqs == 0) return KARA_OK;
+  if (!q_window || !kv_pool || !block_table_d || !seq_lens_d || !new_block_table_d)
+    return fail(KARA_E_INVAL, "device pointer NULL");
+  if (!is_aligned(q_window, 16) || !is_aligned(kv_pool, 16))
+    return fail(KARA_E_INVAL, "q_window and kv_pool must be 16-byte aligned");
+  const Workspace ws = layout(shape, params, n_seqs);
+  if (!workspace || workspace_bytes < ws.total || !is_aligned(workspace, kAlign))
+    return fail(KARA_E_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned", ws.total);
+  Plan plan;
+  if ((st = make_plan(shape, params, n_seqs, block_table_h, max_blocks, seq_lens_h, pool,
+                      new_block_table_h, new_seq_lens_h, &plan)) != KARA_OK)
+    return st;
+
+  hipStream_t s = (hipStream_t)stream;
+  char* w = (char*)workspace;
+  float* partials = (float*)(w + ws.partials);
+  float* scores = scores_out_d;
+  int32_t* retained = retained_out_d ? retained_out_d : (int32_t*)(w + ws.retained);
+  hipError_t e = hipMemcpyAsync(new_block_table_d, new_block_table_h,
+                                (size_t)n_seqs * max_blocks * sizeof(int32_t), hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return hip_fail(e, "block table upload");
+  kara::ScoreArgs sa = score_args(shape, params, n_seqs, q_window, kv_pool, n_blocks, block_table_d,
+                                  max_blocks, seq_lens_d, partials);
+  if ((e = kara::launch_score(sa, shape->dtype, s)) != hipSuccess) return hip_fail(e, "score launch");
+  kara::SelectArgs se;
+  se.partials = partials;
+  se.n_split = sa.n_split;
+  se.cand_in = nullptr;
+  se.scores_out = scores;
+  se.cand_out = cand_out_d;
+  se.retained_out = retained;
+  se.n_units = sa.n_units;
+  se.C = sa.C;
+  se.K = params->top_k;
+  se.R = params->budget;
+  se.mode = kara::kSelectFull;
+  if ((e = kara::launch_select(se, s)) != hipSuccess) return hip_fail(e, "select launch");
+  kara::CompactArgs ca = compact_args(shape, params, n_seqs, kv_pool, n_blocks, block_table_d,
+                                      new_block_table_d, max_blocks, seq_lens_d, retained);
+  if ((e = kara::launch_compact(ca, s)) != hipSuccess) return hip_fail(e, "compact launch");
+  commit_plan(pool, plan);
+  return KARA_OK;
+}
+
+kara_status kara_score(const kara_shape* shape, const kara_params* params, int32_t n_seqs,
+                       const void* q_window, const void* kv_pool, int32_t n_blocks,
+                       const int32_t* block_table_h, const int32_t* block_table_d, int32_t max_blocks,
+                       const int32_t* seq_lens_h, const int32_t* seq_lens_d, float* scores_d,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  kara_status st;
+  if ((st = check_shape(shape)) != KARA_OK) return st;
+  if ((st = check_params(params)) != KARA_OK) return st;
+  if ((st = check_sequences(shape, params, n_seqs, n_blocks, block_table_h, max_blocks, seq_lens_h, nullptr)) != KARA_OK)
+    return st;
+  if (n_seqs == 0) return KARA_OK;
+  if (!q_window || !kv_pool || !block_table_d || !seq_lens_d || !scores_d)
+    return fail(KARA_E_INVAL, "device pointer NULL");
+  if (!is_aligned(q_window, 16) || !is_aligned(kv_pool, 16))
+    return fail(KARA_E_INVAL, "q_window and kv_pool must be 16-byte aligned");
+  const Workspace ws = layout(shape, params, n_seqs);
+  const int G = shape->n_q_heads / shape->n_kv_heads;
+  const bool direct = kara::score_chunks(G, params->window) == 1;
+  if (!direct && (!workspace || workspace_bytes < ws.retained || !is_aligned(workspace, kAlign)))
+    return fail(KARA_E_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned", ws.retained);
+  hipStream_t s = (hipStream_t)stream;
+  float* partials = direct ? scores_d : (float*)((char*)workspace + ws.partials);
+  kara::ScoreArgs sa = score_args(shape, params, n_seqs, q_window, kv_pool, n_blocks, block_table_d,
+                                  max_blocks, seq_lens_d, partials);
+  hipError_t e = kara::launch_score(sa, shape->dtype, s);
+  if (e != hipSuccess) return hip_fail(e, "score launch");
+  if (!direct && (e = kara::launch_reduce(partials, scores_d, sa.n_units, sa.n_split, sa.C, s)) != hipSuccess)
+    return hip_fail(e, "reduce launch");
+  return KARA_OK;
+}
+
+kara_status kara_topk(int32_t n_units, int32_t region, int32_t top_k, const float* scores_d,
+                      int32_t* cand_d, void* stream) {
+  if (n_units < 0) return fail(KARA_E_INVAL, "n_units < 0");
+  if (region < 1 || region > kara::kMaxRegion) return fail(KARA_E_INVAL, "region %d outside [1, %d]", region, kara::kMaxRegion);
+  if (top_k < 1 || top_k > region) return fail(KARA_E_INVAL, "top_k %d outside [1, %d]", top_k, region);
+  if (n_units == 0) return KARA_OK;
+  if (!scores_d || !cand_d) return fail(KARA_E_INVAL, "device pointer NULL");
+  kara::SelectArgs se;
+  se.partials = scores_d;
+  se.n_split = 1;
+  se.cand_in = nullptr;
+  se.scores_out = nullptr;
+  se.cand_out = cand_d;
+  se.retained_out = nullptr;
+  se.n_units = n_units;
+  se.C = region;
+  se.K = top_k;
+  se.R = top_k;
+  se.mode = kara::kSelectTopK;
+  hipError_t e = kara::launch_select(se, (hipStream_t)stream);
+  return e == hipSuccess ? KARA_OK : hip_fail(e, "topk launch");
+}
+
+kara_status kara_token2chunk(int32_t n_units, int32_t region, int32_t top_k, int32_t budget,
+                             const float* scores_d, const int32_t* cand_d, int32_t* retained_d,
+                             void* stream) {
+  if (n_units < 0) return fail(KARA_E_INVAL, "n_units < 0");
+  if (region < 1 || region > kara::kMaxRegion) return fail(KARA_E_INVAL, "region %d outside [1, %d]", region, kara::kMaxRegion);
+  if (top_k < 1 || top_k > region) return fail(KARA_E_INVAL, "top_k %d outside [1, %d]", top_k, region);
+  if (budget < 1 || budget > region) return fail(KARA_E_INVAL, "budget %d outside [1, %d]", budget, region);
+  if (n_units == 0) return KARA_OK;
+  if (!scores_d || !cand_d || !retained_d) return fail(KARA_E_INVAL, "device pointer NULL");
+  kara::SelectArgs se;
+  se.partials = scores_d;
+  se.n_split = 1;
+  se.cand_in = cand_d;
+  se.scores_out = nullptr;
+  se.cand_out = nullptr;
+  se.retained_out = retained_d;
+  se.n_units = n_units;
+  se.C = region;
+  se.K = top_k;
+  se.R = budget;
+  se.mode = kara::kSelectT2C;
+  hipError_t e = kara::launch_select(se, (hipStream_t)stream);
+  return e == hipSuccess ? KARA_OK : hip_fail(e, "token2chunk launch");
+}
+
+kara_status kara_paged_compact(const kara_shape* shape, const kara_params* params, int32_t n_seqs,
+                               void* kv_pool, int32_t n_blocks, const int32_t* block_table_h,
+                               const int32_t* block_table_d, int32_t max_blocks,
+                               const int32_t* seq_lens_h, const int32_t* seq_lens_d,
+                               const int32_t* retained_d, kara_pool* pool, int32_t* new_block_table_h,
+                               int32_t* new_block_table_d, int32_t* new_seq_lens_h, void* stream) {
+  kara_status st;
+  if ((st = check_shape(shape)) != KARA_OK) return st;
+  if ((st = check_params(params)) != KARA_OK) return st;
+  if (!pool) return fail(KARA_E_INVAL, "pool is NULL");
+  if (pool->n_blocks != n_blocks) return fail(KARA_E_INVAL, "pool covers %d blocks, cache has %d", pool->n_blocks, n_blocks);
+  if ((st = check_sequences(shape, params, n_seqs, n_blocks, block_table_h, max_blocks, seq_lens_h, pool)) != KARA_OK)
+    return st;
+  if (n_seqs == 0) return KARA_OK;
+  if (!kv_pool || !block_table_d || !seq_lens_d || !retained_d || !new_block_table_d)
+    return fail(KARA_E_INVAL, "device pointer NULL");
+  if (!is_aligned(kv_pool, 16)) return fail(KARA_E_INVAL, "kv_pool must be 16-byte aligned");
+  Plan plan;
+  if ((st = make_plan(shape, params, n_seqs, block_table_h, max_blocks, seq_lens_h, pool,
+                      new_block_table_h, new_seq_lens_h, &plan)) != KARA_OK)
+    return st;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(new_block_table_d, new_block_table_h,
+                                (size_t)n_seqs * max_blocks * sizeof(int32_t), hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return hip_fail(e, "block table upload");
+  kara::CompactArgs ca = compact_args(shape, params, n_seqs, kv_pool, n_blocks, block_table_d,
+                                      new_block_table_d, max_blocks, seq_lens_d, retained_d);
+  if ((e = kara::launch_compact(ca, s)) != hipSuccess) return hip_fail(e, "compact launch");
+  commit_plan(pool, plan);
+  return KARA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,65 @@
+// Internal launch interface between the C ABI front end (kara_api.cpp) and the
+// gfx950 kernels.  Not installed; the public surface is include/kara.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace kara {
+
+constexpr int kMaxWindow = 4096;
+constexpr int kMaxRegion = 2048;
+
+// Rows (query-head x window-position pairs) scored by one workgroup of the
+// score kernel: 8 waves x 64 rows.
+constexpr int kScoreRowsPerChunk = 512;
+
+struct ScoreArgs {
+  const void* q;          // [S][Lyr][W][Hq][D]
+  const void* pool;       // [Lyr][2][NB][Hkv][bs][D]
+  const int32_t* table;   // [S][MB]
+  const int32_t* lens;    // [S]
+  float* out;             // [U][n_split][C]: partial column sums of each row chunk
+  int S, Lyr, Hq, Hkv, G, D, bs, NB, MB, W, C;
+  int n_split;            // row chunks per unit = ceil(G*W / kScoreRowsPerChunk)
+  int n_units;            // S * Lyr * Hkv
+  float c;                // log2(e) / sqrt(D)
+};
+
+inline int score_chunks(int G, int W) {
+  return (G * W + kScoreRowsPerChunk - 1) / kScoreRowsPerChunk;
+}
+
+hipError_t launch_score(const ScoreArgs& a, int dtype, hipStream_t stream);
+
+// Sums the n_split partial rows of every unit (in chunk order) into scores.
+hipError_t launch_reduce(const float* partials, float* scores, int n_units, int n_split, int C,
+                         hipStream_t stream);
+
+enum SelectMode { kSelectTopK = 0, kSelectT2C = 1, kSelectFull = 2 };
+
+struct SelectArgs {
+  const float* partials;  // [U][n_split][C]; unit scores are the chunk-ordered sums
+  int n_split;
+  const int32_t* cand_in; // [U][K] (kSelectT2C only)
+  float* scores_out;      // optional [U][C]
+  int32_t* cand_out;      // optional [U][K]
+  int32_t* retained_out;  // [U][R] (kSelectT2C / kSelectFull)
+  int n_units, C, K, R;
+  int mode;
+};
+
+hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
+
+struct CompactArgs {
+  void* pool;                 // [Lyr][2][NB][Hkv][bs][D]
+  const int32_t* old_table;   // [S][MB]
+  const int32_t* new_table;   // [S][MB]
+  const int32_t* lens;        // [S] (old lengths)
+  const int32_t* retained;    // [S][Lyr][Hkv][R]
+  int S, Lyr, Hkv, row_bytes, bs, NB, MB, W, B, R;
+};
+
+hipError_t launch_compact(const CompactArgs& a, hipStream_t stream);
+
+}  // namespace kara

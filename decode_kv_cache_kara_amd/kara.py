@@ -1,0 +1,245 @@
+"""ctypes binding of libkara.so (include/kara.h).  Argument marshalling only:
+every step of the compression runs in the library's HIP kernels.
+
+Each C entry point has a Python function of the same name.  Device buffers are
+torch tensors on the GPU, host buffers torch tensors on the CPU; their pointers
+are passed as they are (no copies, no conversions).  A non-OK status raises
+KaraError carrying the status and the library's message.  If libkara.so is
+missing the import fails: there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkara.so")
+
+KARA_OK = 0
+KARA_E_INVAL = 1
+KARA_E_NOBLOCKS = 2
+KARA_E_HIP = 3
+KARA_E_UNSUPPORTED = 4
+KARA_E_WORKSPACE = 5
+KARA_F32 = 0
+KARA_BF16 = 1
+
+STATUS_NAMES = {0: "KARA_OK", 1: "KARA_E_INVAL", 2: "KARA_E_NOBLOCKS", 3: "KARA_E_HIP",
+                4: "KARA_E_UNSUPPORTED", 5: "KARA_E_WORKSPACE"}
+
+
+class KaraError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+class kara_shape(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class kara_params(ctypes.Structure):
+    _fields_ = [("window", ctypes.c_int32), ("protect", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("budget", ctypes.c_int32)]
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_SIGS = {
+    "kara_last_error": (ctypes.c_char_p, []),
+    "kara_version": (ctypes.c_char_p, []),
+    "kara_pool_create": (_I, [_I, _P, _I, ctypes.POINTER(_P)]),
+    "kara_pool_alloc": (_I, [_P, _I, _P]),
+    "kara_pool_free": (_I, [_P, _P, _I]),
+    "kara_pool_num_free": (_I, [_P]),
+    "kara_pool_snapshot": (_I, [_P, _P, _I]),
+    "kara_pool_destroy": (None, [_P]),
+    "kara_workspace_bytes": (ctypes.c_size_t, [_P, _P, _I]),
+    "kara_compress": (_I, [_P, _P, _I, _P, _P, _I, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P,
+                           ctypes.c_size_t, _P, _P, _P, _P]),
+    "kara_score": (_I, [_P, _P, _I, _P, _P, _I, _P, _P, _I, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "kara_topk": (_I, [_I, _I, _I, _P, _P, _P]),
+    "kara_token2chunk": (_I, [_I, _I, _I, _I, _P, _P, _P, _P]),
+    "kara_paged_compact": (_I, [_P, _P, _I, _P, _I, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
+}
+EXPORTED = tuple(_SIGS)
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m decode_kv_cache_kara_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+lib = _lib  # raw ctypes handle, for callers that marshal pointers themselves
+
+
+def _check(status):
+    if status != KARA_OK:
+        raise KaraError(status, _lib.kara_last_error().decode())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _host_i32(t, name):
+    if t.device.type != "cpu" or t.dtype != torch.int32 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous int32 CPU tensor")
+    return t.data_ptr()
+
+
+def _dev(t, name, dtype=None):
+    if t is None:
+        return None
+    if t.device.type != "cuda" or not t.is_contiguous() or (dtype is not None and t.dtype != dtype):
+        raise ValueError(f"{name} must be a contiguous {dtype or ''} GPU tensor")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def dtype_code(dtype):
+    if dtype == torch.bfloat16:
+        return KARA_BF16
+    if dtype == torch.float32:
+        return KARA_F32
+    raise ValueError(f"unsupported dtype {dtype}")
+
+
+def kara_version():
+    return _lib.kara_version().decode()
+
+
+def kara_last_error():
+    return _lib.kara_last_error().decode()
+
+
+class Pool:
+    """A library-owned FIFO free list of block ids (kara_pool)."""
+
+    def __init__(self, n_blocks, free_ids):
+        if isinstance(free_ids, torch.Tensor):
+            ids = free_ids.to(torch.int32).contiguous().cpu()
+        else:
+            ids = torch.tensor(list(free_ids), dtype=torch.int32)
+        h = _P()
+        _check(_lib.kara_pool_create(int(n_blocks), ids.data_ptr() if len(ids) else None, len(ids),
+                                     ctypes.byref(h)))
+        self.handle = h
+        self.n_blocks = int(n_blocks)
+
+    def alloc(self, n):
+        out = torch.empty(n, dtype=torch.int32)
+        _check(_lib.kara_pool_alloc(self.handle, int(n), out.data_ptr() if n else None))
+        return out.tolist()
+
+    def free(self, ids):
+        t = torch.tensor(list(ids), dtype=torch.int32)
+        _check(_lib.kara_pool_free(self.handle, t.data_ptr() if len(t) else None, len(t)))
+
+    def num_free(self):
+        return int(_lib.kara_pool_num_free(self.handle))
+
+    def snapshot(self):
+        n = self.num_free()
+        out = torch.empty(max(n, 1), dtype=torch.int32)
+        k = _lib.kara_pool_snapshot(self.handle, out.data_ptr(), n)
+        return out[:k].tolist()
+
+    def close(self):
+        if self.handle:
+            _lib.kara_pool_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def kara_workspace_bytes(shape, params, n_seqs):
+    return int(_lib.kara_workspace_bytes(ctypes.byref(shape), ctypes.byref(params), int(n_seqs)))
+
+
+def kara_compress(shape, params, q_window, kv_pool, block_table_h, block_table_d, seq_lens_h,
+                  seq_lens_d, pool, new_block_table_h, new_block_table_d, new_seq_lens_h,
+                  workspace, stream=None, scores_out=None, cand_out=None, retained_out=None):
+    n_seqs = seq_lens_h.numel()
+    _check(_lib.kara_compress(
+        ctypes.byref(shape), ctypes.byref(params), n_seqs, _dev(q_window, "q_window"),
+        _dev(kv_pool, "kv_pool"), kv_pool.shape[2], _host_i32(block_table_h, "block_table_h"),
+        _dev(block_table_d, "block_table_d", torch.int32), block_table_h.shape[1],
+        _host_i32(seq_lens_h, "seq_lens_h"), _dev(seq_lens_d, "seq_lens_d", torch.int32),
+        pool.handle, _host_i32(new_block_table_h, "new_block_table_h"),
+        _dev(new_block_table_d, "new_block_table_d", torch.int32),
+        _host_i32(new_seq_lens_h, "new_seq_lens_h"), _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size() if workspace is not None else 0,
+        _stream(stream), _dev(scores_out, "scores_out", torch.float32),
+        _dev(cand_out, "cand_out", torch.int32), _dev(retained_out, "retained_out", torch.int32)))
+
+
+def kara_score(shape, params, q_window, kv_pool, block_table_h, block_table_d, seq_lens_h,
+               seq_lens_d, scores_out, workspace, stream=None):
+    n_seqs = seq_lens_h.numel()
+    _check(_lib.kara_score(
+        ctypes.byref(shape), ctypes.byref(params), n_seqs, _dev(q_window, "q_window"),
+        _dev(kv_pool, "kv_pool"), kv_pool.shape[2], _host_i32(block_table_h, "block_table_h"),
+        _dev(block_table_d, "block_table_d", torch.int32), block_table_h.shape[1],
+        _host_i32(seq_lens_h, "seq_lens_h"), _dev(seq_lens_d, "seq_lens_d", torch.int32),
+        _dev(scores_out, "scores_out", torch.float32), _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size() if workspace is not None else 0,
+        _stream(stream)))
+
+
+def kara_topk(scores, top_k, cand_out, stream=None):
+    n_units, region = scores.shape
+    _check(_lib.kara_topk(n_units, region, int(top_k), _dev(scores, "scores", torch.float32),
+                          _dev(cand_out, "cand_out", torch.int32), _stream(stream)))
+
+
+def kara_token2chunk(scores, cand, budget, retained_out, stream=None):
+    n_units, region = scores.shape
+    _check(_lib.kara_token2chunk(n_units, region, cand.shape[1], int(budget),
+                                 _dev(scores, "scores", torch.float32),
+                                 _dev(cand, "cand", torch.int32),
+                                 _dev(retained_out, "retained_out", torch.int32), _stream(stream)))
+
+
+def kara_paged_compact(shape, params, kv_pool, block_table_h, block_table_d, seq_lens_h, seq_lens_d,
+                       retained, pool, new_block_table_h, new_block_table_d, new_seq_lens_h,
+                       stream=None):
+    n_seqs = seq_lens_h.numel()
+    _check(_lib.kara_paged_compact(
+        ctypes.byref(shape), ctypes.byref(params), n_seqs, _dev(kv_pool, "kv_pool"),
+        kv_pool.shape[2], _host_i32(block_table_h, "block_table_h"),
+        _dev(block_table_d, "block_table_d", torch.int32), block_table_h.shape[1],
+        _host_i32(seq_lens_h, "seq_lens_h"), _dev(seq_lens_d, "seq_lens_d", torch.int32),
+        _dev(retained, "retained", torch.int32), pool.handle,
+        _host_i32(new_block_table_h, "new_block_table_h"),
+        _dev(new_block_table_d, "new_block_table_d", torch.int32),
+        _host_i32(new_seq_lens_h, "new_seq_lens_h"), _stream(stream)))

@@ -1,0 +1,225 @@
+/*
+ * kara.h - C ABI of the Kara decode-time KV-cache compression step on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The step, per sequence b, layer l and KV head h ("unit"), over the trailing
+ * window of W tokens of the sequence:
+ *   1. score   every key j < C = W - B of the window by the softmax attention
+ *              that ALL W window queries of the head's query group give it,
+ *              each softmax over all W window keys with no causal mask;
+ *   2. top-K   keep the K best-scored keys as candidates;
+ *   3. chunks  expand gaps between consecutive candidates into chunks, filling
+ *              a budget of R kept tokens of the region;
+ *   4. compact copy the kept K/V rows into fresh blocks of the paged cache and
+ *              return the sequence's old trailing blocks to the free pool.
+ * Sources: "Technical Summary: Kara - Sliding-Window KV Cache Compression for
+ * Efficient Serving of Reasoning LLMs" (gist.science), Methodology 1
+ * (Mechanism, Rationale, Selection), 2 (Process, Outcome) and 3 (Periodic
+ * Compression Policy); the paper's Abstract (decoding-time compression of the
+ * recently generated context; expanding a subset of the selected pairs into
+ * chunks; adaptation to PagedAttention).
+ *
+ * Readings this library fixes where the pages are silent: softmax scale
+ * 1/sqrt(D); query head q belongs to KV head q / G (G = Hq / Hkv); Top-K ties
+ * go to the lower position; chunk score (s[a] + s[b]) / (g + 2) for
+ * consecutive candidates a < b with g = b - a - 1 > 0, computed in float32
+ * (round-to-nearest add, then divide); chunks accepted as the longest prefix of
+ * the (score desc, left endpoint asc) order whose gaps fit in R - K; the
+ * highest-scored remaining positions (ties to the lower position) top the set
+ * up to exactly R; if R < K the kept set is the top-R set.  Every (layer, head)
+ * thus keeps exactly R tokens, so one block table and one length per sequence
+ * stay valid and the new lengths are known on the host before any kernel runs.
+ *
+ * Memory layouts (row-major, innermost last):
+ *   q_window  [n_seqs][n_layers][W][n_q_heads][head_dim]            (dtype)
+ *   kv_pool   [n_layers][2][n_blocks][n_kv_heads][block_size][head_dim]
+ *             index 1 of the second axis: 0 = K, 1 = V                 (dtype)
+ *   tables    [n_seqs][max_blocks] int32 block ids
+ *   scores    [n_seqs][n_layers][n_kv_heads][C] float32
+ *   cand      [n_seqs][n_layers][n_kv_heads][K] int32, ascending
+ *   retained  [n_seqs][n_layers][n_kv_heads][R] int32, ascending, in [0, C)
+ * Window-local position i of sequence b is token lens[b] - W + i.
+ *
+ * Ownership: the caller owns every buffer and the stream.  The library never
+ * allocates device memory; kara_compress and kara_score use a caller-provided
+ * device workspace of kara_workspace_bytes() bytes.  A kara_pool is host
+ * memory owned by the library between kara_pool_create and kara_pool_destroy.
+ * "dev" pointers are device memory, "host" pointers host memory.
+ *
+ * Errors: every entry point validates all of its arguments before any side
+ * effect.  A non-OK status from validation means nothing changed (pool, host
+ * outputs and device memory are untouched).  KARA_E_HIP means a HIP call
+ * failed after validation; work already enqueued may have run and the stream
+ * should be treated as poisoned.  kara_last_error() returns a message for the
+ * last non-OK status of the calling thread.
+ *
+ * Ordering: kernels are enqueued on `stream` (a hipStream_t; NULL is the null
+ * stream) and the calls return without waiting for them.  Host outputs are
+ * valid on return; device outputs are valid once the stream reaches the call.
+ * Entry points are not thread-safe with respect to the same kara_pool.
+ */
+#ifndef KARA_H
+#define KARA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KARA_OK = 0,
+  KARA_E_INVAL = 1,        /* invalid argument; nothing changed */
+  KARA_E_NOBLOCKS = 2,     /* the free pool holds too few blocks; nothing changed */
+  KARA_E_HIP = 3,          /* a HIP runtime call failed after validation */
+  KARA_E_UNSUPPORTED = 4,  /* shape or dtype the kernels are not built for; nothing changed */
+  KARA_E_WORKSPACE = 5     /* workspace NULL or smaller than kara_workspace_bytes(); nothing changed */
+} kara_status;
+
+typedef enum { KARA_F32 = 0, KARA_BF16 = 1 } kara_dtype;
+
+/* Model and cache geometry.  Supported: head_dim 64 or 128; n_q_heads a
+ * multiple of n_kv_heads; block_size >= 1; dtype KARA_F32 or KARA_BF16. */
+typedef struct {
+  int32_t n_layers;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t dtype;           /* kara_dtype */
+} kara_shape;
+
+/* Method parameters: window W, protected buffer B, candidates K, budget R.
+ * Valid: 1 <= W <= 4096, 0 <= B < W, C = W - B <= 2048, 1 <= K <= C,
+ * 1 <= R <= C. */
+typedef struct {
+  int32_t window;
+  int32_t protect;
+  int32_t top_k;
+  int32_t budget;
+} kara_params;
+
+/* Host free list of block ids: allocation pops the front, freeing pushes the
+ * back (first in, first out), so block assignment is deterministic. */
+typedef struct kara_pool kara_pool;
+
+/* Message for the calling thread's last non-OK status ("" if none). */
+const char* kara_last_error(void);
+
+/* Library version string. */
+const char* kara_version(void);
+
+/* Creates a pool over ids [0, n_blocks) whose free list is free_ids[0..n_free)
+ * in that order (front first).  Ids must be in range and distinct.
+ * KARA_E_INVAL on bad arguments (*out untouched). */
+kara_status kara_pool_create(int32_t n_blocks, const int32_t* free_ids, int32_t n_free,
+                             kara_pool** out);
+
+/* Pops n ids from the front into ids_out[0..n).  KARA_E_NOBLOCKS if fewer than
+ * n are free (nothing popped). */
+kara_status kara_pool_alloc(kara_pool* pool, int32_t n, int32_t* ids_out);
+
+/* Pushes ids[0..n) to the back, in order.  KARA_E_INVAL if an id is out of
+ * range, already free or repeated (nothing pushed). */
+kara_status kara_pool_free(kara_pool* pool, const int32_t* ids, int32_t n);
+
+/* Number of free ids. */
+int32_t kara_pool_num_free(const kara_pool* pool);
+
+/* Copies up to cap free ids, front first, into ids_out; returns how many. */
+int32_t kara_pool_snapshot(const kara_pool* pool, int32_t* ids_out, int32_t cap);
+
+void kara_pool_destroy(kara_pool* pool);
+
+/* Device workspace bytes that kara_compress and kara_score need for n_seqs
+ * sequences of this shape (0 on invalid arguments). */
+size_t kara_workspace_bytes(const kara_shape* shape, const kara_params* params, int32_t n_seqs);
+
+/* Whole step for n_seqs sequences (the selected ones, in call order).
+ *
+ * q_window       dev   window query states (layout above), dtype of shape.
+ * kv_pool        dev   K/V pool; the kept rows are written into fresh blocks.
+ *                      Rows of all other blocks are not written.
+ * n_blocks             blocks in the pool.
+ * block_table_h  host  [n_seqs][max_blocks]; entries of positions
+ *                      (lens[b]-W)/bs .. ceil(lens[b]/bs)-1 must be distinct
+ *                      valid ids not in the free list; earlier entries are
+ *                      copied unchanged and never read.
+ * block_table_d  dev   device copy of block_table_h (same contents).
+ * seq_lens_h     host  [n_seqs] lengths, each >= W and <= max_blocks * bs.
+ * seq_lens_d     dev   device copy of seq_lens_h.
+ * pool                 free list; on success the fresh blocks (sum over b of
+ *                      ceil((p_b + R + B) / bs), p_b = (lens[b] - W) mod bs)
+ *                      are popped, sequences in call order, and then the old
+ *                      blocks of positions (lens[b]-W)/bs .. ceil(lens[b]/bs)-1
+ *                      are pushed, sequences in call order and positions
+ *                      ascending.  Reuse of a pushed block is safe for work
+ *                      enqueued later on the same stream.
+ * new_block_table_h host out [n_seqs][max_blocks]: positions before the
+ *                      boundary block unchanged, then the fresh ids, then -1.
+ * new_block_table_d dev out, filled by a stream-ordered copy of
+ *                      new_block_table_h (pinned host memory must stay
+ *                      unchanged until the stream passes the call).
+ * new_seq_lens_h host out [n_seqs]: lens[b] - C + R.
+ * workspace      dev   kara_workspace_bytes() bytes, 256-byte aligned.
+ * stream               hipStream_t.
+ * scores_out_d, cand_out_d, retained_out_d   optional dev outputs (NULL: not
+ *                      written) in the layouts above.
+ * Errors: KARA_E_INVAL, KARA_E_UNSUPPORTED, KARA_E_WORKSPACE, KARA_E_NOBLOCKS
+ * (all with nothing changed), KARA_E_HIP. */
+kara_status kara_compress(const kara_shape* shape, const kara_params* params, int32_t n_seqs,
+                          const void* q_window, void* kv_pool, int32_t n_blocks,
+                          const int32_t* block_table_h, const int32_t* block_table_d,
+                          int32_t max_blocks, const int32_t* seq_lens_h,
+                          const int32_t* seq_lens_d, kara_pool* pool,
+                          int32_t* new_block_table_h, int32_t* new_block_table_d,
+                          int32_t* new_seq_lens_h, void* workspace, size_t workspace_bytes,
+                          void* stream, float* scores_out_d, int32_t* cand_out_d,
+                          int32_t* retained_out_d);
+
+/* Stage 1 alone: window scores of every unit into scores_d (dev, [n_seqs]
+ * [n_layers][n_kv_heads][C] float32).  Arguments as for kara_compress;
+ * top_k and budget are validated but unused.  Summary, Methodology 1
+ * (Mechanism, Rationale). */
+kara_status kara_score(const kara_shape* shape, const kara_params* params, int32_t n_seqs,
+                       const void* q_window, const void* kv_pool, int32_t n_blocks,
+                       const int32_t* block_table_h, const int32_t* block_table_d,
+                       int32_t max_blocks, const int32_t* seq_lens_h, const int32_t* seq_lens_d,
+                       float* scores_d, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Stage 2 alone: for each of n_units rows of `region` float32 scores (dev,
+ * finite), the top_k positions with the largest score (ties to the lower
+ * position, -0 equal to +0), ascending, into cand_d (dev [n_units][top_k]).
+ * Summary, Methodology 1 (Selection).  1 <= top_k <= region <= 2048. */
+kara_status kara_topk(int32_t n_units, int32_t region, int32_t top_k, const float* scores_d,
+                      int32_t* cand_d, void* stream);
+
+/* Stage 3 alone: Token2Chunk of each unit from its scores (dev [n_units]
+ * [region]) and ascending candidates (dev [n_units][top_k], strictly
+ * increasing, in [0, region)), into retained_d (dev [n_units][budget]).
+ * Summary, Methodology 2 (Process, Outcome).  1 <= budget <= region.
+ * Candidates that break the stated form give an unspecified (but in-range,
+ * fault-free) result. */
+kara_status kara_token2chunk(int32_t n_units, int32_t region, int32_t top_k, int32_t budget,
+                             const float* scores_d, const int32_t* cand_d, int32_t* retained_d,
+                             void* stream);
+
+/* Stage 4 alone: the bookkeeping and copy of kara_compress for given kept
+ * positions retained_d (dev [n_seqs][n_layers][n_kv_heads][R], ascending in
+ * [0, C); out-of-range entries are clamped, never dereferenced out of
+ * bounds).  Pool, tables and lengths as for kara_compress.  Summary,
+ * Methodology 3 (Periodic Compression Policy: trailing blocks). */
+kara_status kara_paged_compact(const kara_shape* shape, const kara_params* params, int32_t n_seqs,
+                               void* kv_pool, int32_t n_blocks, const int32_t* block_table_h,
+                               const int32_t* block_table_d, int32_t max_blocks,
+                               const int32_t* seq_lens_h, const int32_t* seq_lens_d,
+                               const int32_t* retained_d, kara_pool* pool,
+                               int32_t* new_block_table_h, int32_t* new_block_table_d,
+                               int32_t* new_seq_lens_h, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KARA_H */

@@ -1,0 +1,171 @@
+"""Host-side tests of libkara.so that need no GPU: every symbol of
+include/kara.h is exported, the FIFO pool behaves as documented, and invalid
+arguments are rejected before anything is touched (the device pointers passed
+here are never valid, so any dereference would crash)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from decode_kv_cache_kara_amd import kara
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10  # never dereferenced: validation fails first
+
+
+def header_functions():
+    with open(os.path.join(ROOT, "include", "kara.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"\b(kara_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(kara.LIB_PATH)
+    names = header_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(kara.EXPORTED)
+
+
+def test_version():
+    assert "gfx950" in kara.kara_version()
+
+
+def test_pool_fifo():
+    p = kara.Pool(10, [7, 3, 5, 1])
+    assert p.num_free() == 4
+    assert p.alloc(2) == [7, 3]
+    p.free([9, 0])
+    assert p.snapshot() == [5, 1, 9, 0]
+    with pytest.raises(kara.KaraError) as e:
+        p.alloc(5)
+    assert e.value.status == kara.KARA_E_NOBLOCKS
+    assert p.snapshot() == [5, 1, 9, 0]
+
+
+@pytest.mark.parametrize("ids", [[1, 1], [5], [10], [-1]])
+def test_pool_free_rejects(ids):
+    p = kara.Pool(10, [5, 6])
+    with pytest.raises(kara.KaraError) as e:
+        p.free(ids)
+    assert e.value.status == kara.KARA_E_INVAL
+    assert p.snapshot() == [5, 6]
+
+
+@pytest.mark.parametrize("n,ids", [(0, []), (4, [0, 0]), (4, [4]), (4, [-2])])
+def test_pool_create_rejects(n, ids):
+    with pytest.raises(kara.KaraError):
+        kara.Pool(n, ids)
+
+
+def shape(**kw):
+    d = dict(n_layers=2, n_q_heads=8, n_kv_heads=2, head_dim=128, block_size=4, dtype=kara.KARA_BF16)
+    d.update(kw)
+    return kara.kara_shape(**d)
+
+
+def params(**kw):
+    d = dict(window=8, protect=2, top_k=2, budget=3)
+    d.update(kw)
+    return kara.kara_params(**d)
+
+
+def test_workspace_bytes():
+    sh, pr = shape(), params()
+    n1 = kara.kara_workspace_bytes(sh, pr, 1)
+    n4 = kara.kara_workspace_bytes(sh, pr, 4)
+    assert 0 < n1 < n4
+    assert kara.kara_workspace_bytes(sh, params(window=0), 1) == 0
+    assert kara.kara_workspace_bytes(shape(head_dim=96), pr, 1) == 0
+
+
+def _i32(vals):
+    return (ctypes.c_int32 * len(vals))(*vals)
+
+
+class Call:
+    """A kara_compress call with valid host arguments and fake device pointers."""
+
+    def __init__(self, **over):
+        self.shape = over.pop("shape", shape())
+        self.params = over.pop("params", params())
+        self.lens = over.pop("lens", [10, 13])
+        bs = self.shape.block_size
+        self.max_blocks = over.pop("max_blocks", 5)
+        self.n_blocks = over.pop("n_blocks", 20)
+        table = over.pop("table", None)
+        if table is None:
+            table, nxt = [], 0
+            for L in self.lens:
+                n = -(-L // bs)
+                row = list(range(nxt, nxt + n)) + [-1] * (self.max_blocks - n)
+                nxt += n
+                table += row
+            free = list(range(nxt, self.n_blocks))
+        else:
+            free = over.pop("free")
+        self.table = _i32(table)
+        self.free = over.pop("free", free)
+        self.pool = kara.Pool(self.n_blocks, self.free)
+        self.new_table = _i32([0] * (len(self.lens) * self.max_blocks))
+        self.new_lens = _i32([0] * len(self.lens))
+        self.ws = over.pop("ws", kara.kara_workspace_bytes(self.shape, self.params, len(self.lens)))
+        assert not over
+
+    def run(self):
+        return kara.lib.kara_compress(
+            ctypes.byref(self.shape), ctypes.byref(self.params), len(self.lens), FAKE * 16, FAKE * 16,
+            self.n_blocks, self.table, FAKE * 16, self.max_blocks, _i32(self.lens), FAKE * 16,
+            self.pool.handle, self.new_table, FAKE * 16, self.new_lens, 256 * 16, self.ws, None,
+            None, None, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(params=params(window=20)), kara.KARA_E_INVAL),            # L < W
+    (dict(params=params(protect=8)), kara.KARA_E_INVAL),            # B >= W
+    (dict(params=params(top_k=7)), kara.KARA_E_INVAL),              # K > C
+    (dict(params=params(budget=0)), kara.KARA_E_INVAL),             # R < 1
+    (dict(params=params(window=5000)), kara.KARA_E_INVAL),
+    (dict(shape=shape(head_dim=96)), kara.KARA_E_UNSUPPORTED),
+    (dict(shape=shape(dtype=7)), kara.KARA_E_UNSUPPORTED),
+    (dict(shape=shape(n_q_heads=7)), kara.KARA_E_INVAL),
+    (dict(table=[0, 1, 2, -1, -1, 3, 4, 25, 5, -1], free=list(range(6, 20))), kara.KARA_E_INVAL),
+    (dict(ws=0), kara.KARA_E_WORKSPACE),
+    (dict(max_blocks=3), kara.KARA_E_INVAL),                        # length needs more blocks
+])
+def test_compress_rejects_before_side_effects(kw, status):
+    c = Call(**kw)
+    before = c.pool.snapshot()
+    assert c.run() == status, kara.kara_last_error()
+    assert kara.kara_last_error()
+    assert c.pool.snapshot() == before
+    assert list(c.new_lens) == [0, 0]
+
+
+def test_compress_pool_exhaustion_changes_nothing():
+    c = Call(n_blocks=8)   # 7 blocks used by the tables, 1 free, 2 x 2 fresh needed
+    before = c.pool.snapshot()
+    assert c.run() == kara.KARA_E_NOBLOCKS
+    assert c.pool.snapshot() == before
+    assert list(c.new_lens) == [0, 0]
+
+
+def test_compress_rejects_duplicate_and_free_blocks():
+    # block 2 appears in both tails
+    c = Call(table=[0, 1, 2, -1, -1, 3, 4, 2, 5, -1], free=list(range(6, 20)))
+    assert c.run() == kara.KARA_E_INVAL
+    # block 4 is in sequence 1's tail and also listed free
+    c = Call(table=[0, 1, 2, -1, -1, 3, 4, 6, 5, -1], free=[4] + list(range(7, 20)))
+    assert c.run() == kara.KARA_E_INVAL
+
+
+def test_stage_entry_points_validate():
+    assert kara.lib.kara_topk(4, 0, 1, FAKE, FAKE, None) == kara.KARA_E_INVAL
+    assert kara.lib.kara_topk(4, 10, 11, FAKE, FAKE, None) == kara.KARA_E_INVAL
+    assert kara.lib.kara_topk(4, 3000, 1, FAKE, FAKE, None) == kara.KARA_E_INVAL
+    assert kara.lib.kara_token2chunk(4, 10, 3, 11, FAKE, FAKE, FAKE, None) == kara.KARA_E_INVAL
+    assert kara.lib.kara_token2chunk(-1, 10, 3, 5, FAKE, FAKE, FAKE, None) == kara.KARA_E_INVAL
+    assert kara.lib.kara_topk(0, 10, 3, None, None, None) == kara.KARA_OK     # nothing to do
