@@ -1,0 +1,206 @@
+"""Throughput of Kara's decode-time compression step on one MI355X.
+
+One step = one kara_compress call (window scoring, Top-K, Token2Chunk and
+paged compaction for every sequence of the batch) on a synthetic workload
+resident in HBM.  Prints one JSON line:
+
+  value      window tokens compressed per second (each window token counted
+             once across all layers of the model slice) = n_seqs * W / step time
+  roofline   the scoring kernel (the dominant one) against the bf16 MFMA peak,
+             with algorithmic flops 2 * Hq * W * W * D per (sequence, layer);
+             its duration is measured with HIP events recorded on the call's
+             stream around that kernel inside the timed steps
+  cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP32_MFMA_TFLOPS = 157.3  # MI355X fp32 (the tiny fp32 workload)
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+METRIC = "window tokens compressed/sec per GPU (score+topK+chunk+compact); % MFMA & HBM peak"
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash(name):
+    with open(os.path.join(ROOT, "decode_kv_cache_kara_amd", "csrc", name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(workload):
+    """HBM bytes per launch of the scoring kernel from the committed counter
+    summary, if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"score_kernel_{workload}_pmc.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("source_sha256_16") != kernel_source_hash("kara_score.hip"):
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, n_layers_sample, seed):
+    """Oracle compress() on 1 sequence x n_layers_sample layers of the same
+    shapes, extrapolated to the metric's unit (window tokens of the full
+    model slice per second)."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+
+    from decode_kv_cache_kara_amd import synth
+    from oracle import kara_oracle as ko
+
+    full = synth.CONFIGS[cfg]
+    wl = synth.make_workload(cfg, seed=seed, device="cpu", n_seqs=1, n_layers=n_layers_sample)
+    q = wl.q_window.to(torch.float64).numpy()
+    pool = wl.pool.to(torch.float64).numpy()
+    table = wl.table.long().numpy()
+    lens = wl.lens.long().numpy()
+    t0 = time.perf_counter()
+    ko.compress(q, pool, table, lens, wl.window, wl.protect, wl.top_k, wl.budget, wl.block_size,
+                wl.free_ids)
+    dt = time.perf_counter() - t0
+    frac = n_layers_sample / full["n_layers"]
+    value = wl.window * frac / dt
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": value, "unit": "window tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"oracle compress() (fp64 scores, Top-K, Token2Chunk, pool plan, row gather) on 1 "
+                       f"sequence x {n_layers_sample} of {full['n_layers']} layers of the same shapes "
+                       f"(L={int(lens[0])}), {dt:.1f} s, scaled to the full layer count")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=2, choices=[0, 1, 2, 3])
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-layers", type=int, default=36)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures the compression step on one GPU only; --gpus must be 1 "
+              "(every unit of work is independent, so more GPUs would each run their own batch).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from decode_kv_cache_kara_amd import kara, runner, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    t0 = time.time()
+    wl = synth.make_workload(args.config, seed=args.seed, device="cuda")
+    torch.cuda.synchronize()
+    log(f"workload {wl.name}: {wl.n_seqs} seqs x {wl.n_layers} layers, pool {wl.n_blocks} blocks "
+        f"({wl.pool.numel() * wl.pool.element_size() / 2**30:.1f} GiB), generated in {time.time() - t0:.1f} s")
+    ses = runner.Session(wl, outputs=False)
+    stream = torch.cuda.current_stream()
+
+    def events():
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        for e in ev:
+            e.record(stream)      # materialise the handles
+        return ev
+
+    for _ in range(args.warmup):
+        ses.compress(stream=stream)
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps)")
+
+    step_events = [events() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for k in range(args.steps):
+        ses.compress(stream=stream, stage_events=[e.cuda_event for e in step_events[k]])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / args.steps
+    stage = [0.0, 0.0, 0.0]
+    for ev in step_events:
+        for i in range(3):
+            stage[i] += ev[i].elapsed_time(ev[i + 1])
+    stage = [x / args.steps for x in stage]
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step; score {stage[0]:.3f} ms, "
+        f"select {stage[1]:.3f} ms, compact {stage[2]:.3f} ms")
+
+    S, Lyr, Hq, Hkv, D, W, C = (wl.n_seqs, wl.n_layers, wl.n_q_heads, wl.n_kv_heads, wl.head_dim,
+                                wl.window, wl.region)
+    elt = wl.pool.element_size()
+    tokens = S * W
+    value = tokens / (ms_per_step / 1e3)
+    score_flop = 2.0 * S * Lyr * Hq * W * W * D
+    exec_flop = 2.0 * S * Lyr * Hq * W * (math.ceil(W / 64) * 64 + math.ceil(C / 64) * 64) * D
+    score_tflops = score_flop / (stage[0] / 1e3) / 1e12
+    peak = PEAK_BF16_TFLOPS if wl.dtype == torch.bfloat16 else PEAK_FP32_MFMA_TFLOPS
+    lens = ses.lens_h.tolist()
+    rows = sum(((L - W) % wl.block_size) + wl.budget + wl.protect for L in lens)
+    compact_bytes = 2.0 * rows * Lyr * 2 * Hkv * D * elt
+    compact_gbs = compact_bytes / (stage[2] / 1e3) / 1e9
+    traffic = read_traffic(wl.name)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "window tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic (seeded Gaussian Q/K/V with planted spans; fragmented block tables)",
+        "config": {"workload": wl.name, "n_seqs": S, "n_layers": Lyr, "n_q_heads": Hq, "n_kv_heads": Hkv,
+                   "head_dim": D, "window": W, "protect": wl.protect, "top_k": wl.top_k,
+                   "budget": wl.budget, "block_size": wl.block_size,
+                   "seq_lens": f"U[{min(lens)}..{max(lens)}] seed {wl.seed}"},
+        "roofline": {"bound": "mfma", "kernel": "score_kernel", "achieved": round(score_tflops, 2),
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(score_tflops / peak, 4),
+                     "traffic": traffic, "algorithmic_flop_per_launch": score_flop,
+                     "executed_mfma_flop_per_launch": exec_flop},
+        "stages_ms": {"score": round(stage[0], 4), "select": round(stage[1], 4),
+                      "compact": round(stage[2], 4)},
+        "compact_roofline": {"bound": "hbm", "kernel": "compact_kernel", "achieved": round(compact_gbs, 1),
+                             "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(compact_gbs / PEAK_HBM_GBS, 4),
+                             "algorithmic_bytes_per_launch": compact_bytes},
+    }
+    if not args.no_cpu_baseline:
+        del ses, wl
+        torch.cuda.empty_cache()
+        log("timing the CPU oracle on a sample ...")
+        n_layers_sample = min(args.cpu_layers, synth.CONFIGS[args.config]["n_layers"])
+        out["cpu_baseline"] = cpu_baseline(args.config, n_layers_sample, seed=7)
+        log(f"cpu baseline {out['cpu_baseline']['value']:.1f} window tokens/s")
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

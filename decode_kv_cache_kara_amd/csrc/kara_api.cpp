@@ -311,7 +311,7 @@ kara_status kara_compress(const kara_shape* shape, const kara_params* params, in
                           kara_pool* pool, int32_t* new_block_table_h, int32_t* new_block_table_d,
                           int32_t* new_seq_lens_h, void* workspace, size_t workspace_bytes,
                           void* stream, float* scores_out_d, int32_t* cand_out_d,
-                          int32_t* retained_out_d) {
+                          int32_t* retained_out_d, void* const* stage_events) {
   kara_status st;
   if ((st = check_shape(shape)) != KARA_OK) return st;
   if ((st = check_params(params)) != KARA_OK) return st;
@@ -340,9 +340,14 @@ kara_status kara_compress(const kara_shape* shape, const kara_params* params, in
   hipError_t e = hipMemcpyAsync(new_block_table_d, new_block_table_h,
                                 (size_t)n_seqs * max_blocks * sizeof(int32_t), hipMemcpyHostToDevice, s);
   if (e != hipSuccess) return hip_fail(e, "block table upload");
+  auto mark = [&](int i) -> hipError_t {
+    return stage_events ? hipEventRecord((hipEvent_t)stage_events[i], s) : hipSuccess;
+  };
+  if ((e = mark(0)) != hipSuccess) return hip_fail(e, "stage event");
   kara::ScoreArgs sa = score_args(shape, params, n_seqs, q_window, kv_pool, n_blocks, block_table_d,
                                   max_blocks, seq_lens_d, partials);
   if ((e = kara::launch_score(sa, shape->dtype, s)) != hipSuccess) return hip_fail(e, "score launch");
+  if ((e = mark(1)) != hipSuccess) return hip_fail(e, "stage event");
   kara::SelectArgs se;
   se.partials = partials;
   se.n_split = sa.n_split;
@@ -356,9 +361,11 @@ kara_status kara_compress(const kara_shape* shape, const kara_params* params, in
   se.R = params->budget;
   se.mode = kara::kSelectFull;
   if ((e = kara::launch_select(se, s)) != hipSuccess) return hip_fail(e, "select launch");
+  if ((e = mark(2)) != hipSuccess) return hip_fail(e, "stage event");
   kara::CompactArgs ca = compact_args(shape, params, n_seqs, kv_pool, n_blocks, block_table_d,
                                       new_block_table_d, max_blocks, seq_lens_d, retained);
   if ((e = kara::launch_compact(ca, s)) != hipSuccess) return hip_fail(e, "compact launch");
+  if ((e = mark(3)) != hipSuccess) return hip_fail(e, "stage event");
   commit_plan(pool, plan);
   return KARA_OK;
 }

@@ -61,7 +61,7 @@ _SIGS = {
     "kara_pool_destroy": (None, [_P]),
     "kara_workspace_bytes": (ctypes.c_size_t, [_P, _P, _I]),
     "kara_compress": (_I, [_P, _P, _I, _P, _P, _I, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P,
-                           ctypes.c_size_t, _P, _P, _P, _P]),
+                           ctypes.c_size_t, _P, _P, _P, _P, _P]),
     "kara_score": (_I, [_P, _P, _I, _P, _P, _I, _P, _P, _I, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "kara_topk": (_I, [_I, _I, _I, _P, _P, _P]),
     "kara_token2chunk": (_I, [_I, _I, _I, _I, _P, _P, _P, _P]),
@@ -188,8 +188,11 @@ def kara_workspace_bytes(shape, params, n_seqs):
 
 def kara_compress(shape, params, q_window, kv_pool, block_table_h, block_table_d, seq_lens_h,
                   seq_lens_d, pool, new_block_table_h, new_block_table_d, new_seq_lens_h,
-                  workspace, stream=None, scores_out=None, cand_out=None, retained_out=None):
+                  workspace, stream=None, scores_out=None, cand_out=None, retained_out=None,
+                  stage_events=None):
+    """stage_events: None or 4 raw hipEvent_t handles (ints), see include/kara.h."""
     n_seqs = seq_lens_h.numel()
+    ev = (_P * 4)(*stage_events) if stage_events is not None else None
     _check(_lib.kara_compress(
         ctypes.byref(shape), ctypes.byref(params), n_seqs, _dev(q_window, "q_window"),
         _dev(kv_pool, "kv_pool"), kv_pool.shape[2], _host_i32(block_table_h, "block_table_h"),
@@ -200,7 +203,7 @@ def kara_compress(shape, params, q_window, kv_pool, block_table_h, block_table_d
         _host_i32(new_seq_lens_h, "new_seq_lens_h"), _dev(workspace, "workspace"),
         workspace.numel() * workspace.element_size() if workspace is not None else 0,
         _stream(stream), _dev(scores_out, "scores_out", torch.float32),
-        _dev(cand_out, "cand_out", torch.int32), _dev(retained_out, "retained_out", torch.int32)))
+        _dev(cand_out, "cand_out", torch.int32), _dev(retained_out, "retained_out", torch.int32), ev))
 
 
 def kara_score(shape, params, q_window, kv_pool, block_table_h, block_table_d, seq_lens_h,

@@ -51,12 +51,13 @@ class Session:
     def new_pool(self):
         return kara.Pool(self.wl.n_blocks, self.free_ids)
 
-    def compress(self, stream=None, pool=None):
+    def compress(self, stream=None, pool=None, stage_events=None):
         self.pool = pool if pool is not None else self.new_pool()
         kara.kara_compress(self.shape, self.params, self.wl.q_window, self.wl.pool, self.table_h,
                            self.table_d, self.lens_h, self.lens_d, self.pool, self.new_table_h,
                            self.new_table_d, self.new_lens_h, self.workspace, stream=stream,
-                           scores_out=self.scores, cand_out=self.cand, retained_out=self.retained)
+                           scores_out=self.scores, cand_out=self.cand, retained_out=self.retained,
+                           stage_events=stage_events)
         return self.pool
 
     def score(self, scores_out, stream=None):

@@ -166,6 +166,10 @@ size_t kara_workspace_bytes(const kara_shape* shape, const kara_params* params, 
  * stream               hipStream_t.
  * scores_out_d, cand_out_d, retained_out_d   optional dev outputs (NULL: not
  *                      written) in the layouts above.
+ * stage_events         optional (NULL: none) array of 4 hipEvent_t, recorded
+ *                      on `stream` before the scoring kernel, after it, after
+ *                      the selection kernel and after the compaction kernel,
+ *                      for callers that time the stages.
  * Errors: KARA_E_INVAL, KARA_E_UNSUPPORTED, KARA_E_WORKSPACE, KARA_E_NOBLOCKS
  * (all with nothing changed), KARA_E_HIP. */
 kara_status kara_compress(const kara_shape* shape, const kara_params* params, int32_t n_seqs,
@@ -176,7 +180,7 @@ kara_status kara_compress(const kara_shape* shape, const kara_params* params, in
                           int32_t* new_block_table_h, int32_t* new_block_table_d,
                           int32_t* new_seq_lens_h, void* workspace, size_t workspace_bytes,
                           void* stream, float* scores_out_d, int32_t* cand_out_d,
-                          int32_t* retained_out_d);
+                          int32_t* retained_out_d, void* const* stage_events);
 
 /* Stage 1 alone: window scores of every unit into scores_d (dev, [n_seqs]
  * [n_layers][n_kv_heads][C] float32).  Arguments as for kara_compress;

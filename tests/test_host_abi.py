@@ -120,7 +120,7 @@ class Call:
             ctypes.byref(self.shape), ctypes.byref(self.params), len(self.lens), FAKE * 16, FAKE * 16,
             self.n_blocks, self.table, FAKE * 16, self.max_blocks, _i32(self.lens), FAKE * 16,
             self.pool.handle, self.new_table, FAKE * 16, self.new_lens, 256 * 16, self.ws, None,
-            None, None, None)
+            None, None, None, None)
 
 
 @pytest.mark.parametrize("kw,status", [
