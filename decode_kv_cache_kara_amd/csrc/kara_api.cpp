@@ -44,6 +44,12 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+int log2_exact(int x) {
+  int s = 0;
+  while ((1 << s) < x) ++s;
+  return s;
+}
+
 kara_status check_shape(const kara_shape* sh) {
   if (!sh) return fail(KARA_E_INVAL, "shape is NULL");
   if (sh->n_layers < 1 || sh->n_q_heads < 1 || sh->n_kv_heads < 1 || sh->block_size < 1)
@@ -53,6 +59,8 @@ kara_status check_shape(const kara_shape* sh) {
                 sh->n_q_heads, sh->n_kv_heads);
   if (sh->dtype != KARA_F32 && sh->dtype != KARA_BF16)
     return fail(KARA_E_UNSUPPORTED, "shape: dtype %d not supported", sh->dtype);
+  if (sh->block_size > 1024 || (sh->block_size & (sh->block_size - 1)) != 0)
+    return fail(KARA_E_UNSUPPORTED, "shape: block_size %d is not a power of two <= 1024", sh->block_size);
   if (sh->head_dim != 64 && sh->head_dim != 128)
     return fail(KARA_E_UNSUPPORTED, "shape: head_dim %d not supported (64 or 128)", sh->head_dim);
   return KARA_OK;
@@ -192,6 +200,7 @@ kara::ScoreArgs score_args(const kara_shape* sh, const kara_params* p, int32_t n
   a.G = sh->n_q_heads / sh->n_kv_heads;
   a.D = sh->head_dim;
   a.bs = sh->block_size;
+  a.bs_shift = log2_exact(sh->block_size);
   a.NB = n_blocks;
   a.MB = max_blocks;
   a.W = p->window;

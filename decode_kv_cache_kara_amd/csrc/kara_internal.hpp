@@ -11,8 +11,15 @@ constexpr int kMaxWindow = 4096;
 constexpr int kMaxRegion = 2048;
 
 // Rows (query-head x window-position pairs) scored by one workgroup of the
-// score kernel: 8 waves x 64 rows.
-constexpr int kScoreRowsPerChunk = 512;
+// score kernel, and 32-row query tiles per wave (1: 16 waves of 32 rows).
+#ifndef KARA_ROWS_PER_CHUNK
+#define KARA_ROWS_PER_CHUNK 512
+#endif
+constexpr int kScoreRowsPerChunk = KARA_ROWS_PER_CHUNK;
+#ifndef KARA_ROW_TILES
+#define KARA_ROW_TILES 1
+#endif
+constexpr int kScoreRowTiles = KARA_ROW_TILES;
 
 struct ScoreArgs {
   const void* q;          // [S][Lyr][W][Hq][D]
@@ -20,7 +27,7 @@ struct ScoreArgs {
   const int32_t* table;   // [S][MB]
   const int32_t* lens;    // [S]
   float* out;             // [U][n_split][C]: partial column sums of each row chunk
-  int S, Lyr, Hq, Hkv, G, D, bs, NB, MB, W, C;
+  int S, Lyr, Hq, Hkv, G, D, bs, bs_shift, NB, MB, W, C;
   int n_split;            // row chunks per unit = ceil(G*W / kScoreRowsPerChunk)
   int n_units;            // S * Lyr * Hkv
   float c;                // log2(e) / sqrt(D)
