@@ -86,12 +86,80 @@ def cpu_baseline(cfg, n_layers_sample, seed):
                        f"(L={int(lens[0])}), {dt:.1f} s, scaled to the full layer count")}
 
 
+def run_trace(args, out_base):
+    """Config 4: the periodic-compression serving trace.  A step is one
+    compression event's kara_compress call; `--warmup` events run untimed,
+    then up to `--steps` events (0: all remaining) are timed with HIP events
+    around each call's kernels."""
+    import torch
+
+    from decode_kv_cache_kara_amd.trace import ServingTrace, TraceConfig
+
+    cfg = TraceConfig()
+    t0 = time.time()
+    tr = ServingTrace(cfg)
+    torch.cuda.synchronize()
+    log(f"trace: {cfg.n_seqs} seqs x {cfg.n_layers} layers, {tr.n_events} events, pool {tr.NB} blocks "
+        f"({tr.pool.numel() * 2 / 2**30:.1f} GiB), set up in {time.time() - t0:.1f} s")
+    stream = torch.cuda.current_stream()
+    calls = []
+    n_warm = 0
+    t_start = time.time()
+    while not tr.done():
+        batch = tr.next_event()
+        if not batch:
+            continue
+        q = tr.window_queries(batch)
+        if n_warm < args.warmup:
+            tr.compress(batch, q, stream=stream)
+            n_warm += 1
+            continue
+        if args.steps and len(calls) >= args.steps:
+            tr.compress(batch, q, stream=stream)
+            continue
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        for e in ev:
+            e.record(stream)
+        torch.cuda.synchronize()
+        tr.compress(batch, q, stream=stream, stage_events=[e.cuda_event for e in ev])
+        calls.append((len(batch), ev))
+        if len(calls) % 20 == 0:
+            log(f"event {tr.events}: {len(calls)} timed calls, {time.time() - t_start:.0f} s")
+    torch.cuda.synchronize()
+    total_ms = sum(ev[0].elapsed_time(ev[3]) for _, ev in calls)
+    stage = [sum(ev[i].elapsed_time(ev[i + 1]) for _, ev in calls) for i in range(3)]
+    n_comp = sum(n for n, _ in calls)
+    W = cfg.window
+    value = n_comp * W / (total_ms / 1e3)
+    score_flop = 2.0 * n_comp * cfg.n_layers * cfg.n_q_heads * W * W * cfg.head_dim
+    score_tflops = score_flop / (stage[0] / 1e3) / 1e12
+    log(f"{len(calls)} timed calls, {n_comp} sequence compressions, {total_ms:.1f} ms total")
+    out = dict(out_base)
+    out.update({
+        "value": round(value, 1),
+        "steps": len(calls),
+        "warmup": n_warm,
+        "ms_per_step": round(total_ms / max(len(calls), 1), 4),
+        "data": "synthetic serving trace (seeded decode appends with planted spans, 50% random selection per event)",
+        "config": {"workload": "distill-llama-8b-periodic-trace", "n_seqs": cfg.n_seqs,
+                   "n_layers": cfg.n_layers, "n_q_heads": cfg.n_q_heads, "n_kv_heads": cfg.n_kv_heads,
+                   "head_dim": cfg.head_dim, "window": W, "protect": cfg.protect, "top_k": cfg.top_k,
+                   "budget": cfg.budget, "period": cfg.period, "lengths": f"{cfg.init_len}->{cfg.max_len}",
+                   "events": tr.events, "compressions_timed": n_comp},
+        "roofline": {"bound": "mfma", "kernel": "score_kernel", "achieved": round(score_tflops, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(score_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "algorithmic_flop_total": score_flop},
+        "stages_ms": {"score": round(stage[0], 3), "select": round(stage[1], 3), "compact": round(stage[2], 3)},
+    })
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=2, choices=[0, 1, 2, 3])
+    ap.add_argument("--config", type=int, default=2, choices=[0, 1, 2, 3, 4])
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=36)
@@ -110,6 +178,16 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+
+    if args.config == 4:
+        base = {"metric": METRIC, "unit": "window tokens/s", "n_gpus": 1, "higher_is_better": True,
+                "scaling": "weak", "vs_baseline": None, "dtype": "bf16"}
+        out = run_trace(args, base)
+        if not args.no_cpu_baseline:
+            log("timing the CPU oracle on a sample ...")
+            out["cpu_baseline"] = cpu_baseline(4, min(args.cpu_layers, 32), seed=7)
+        print(json.dumps(out), flush=True)
+        return
 
     t0 = time.time()
     wl = synth.make_workload(args.config, seed=args.seed, device="cuda")

@@ -490,4 +490,23 @@ kara_status kara_paged_compact(const kara_shape* shape, const kara_params* param
   return KARA_OK;
 }
 
+kara_status kara_schedule_step(int64_t step, int32_t period, int32_t window, int32_t n_seqs,
+                               const int32_t* seq_lens, const int32_t* watermarks,
+                               const uint8_t* selected, int32_t* batch_out, int32_t* n_batch) {
+  if (period < 1 || window < 1 || n_seqs < 0 || step < 0 || !n_batch)
+    return fail(KARA_E_INVAL, "bad schedule arguments");
+  if (n_seqs > 0 && (!seq_lens || !watermarks || !selected || !batch_out))
+    return fail(KARA_E_INVAL, "schedule arrays NULL");
+  for (int32_t b = 0; b < n_seqs; ++b)
+    if (watermarks[b] < 0 || watermarks[b] > seq_lens[b])
+      return fail(KARA_E_INVAL, "sequence %d: watermark %d outside [0, %d]", b, watermarks[b], seq_lens[b]);
+  int32_t n = 0;
+  if (step > 0 && step % period == 0) {
+    for (int32_t b = 0; b < n_seqs; ++b)
+      if (selected[b] && (int64_t)seq_lens[b] - watermarks[b] >= window) batch_out[n++] = b;
+  }
+  *n_batch = n;
+  return KARA_OK;
+}
+
 }  // extern "C"

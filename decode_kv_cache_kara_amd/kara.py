@@ -66,6 +66,7 @@ _SIGS = {
     "kara_topk": (_I, [_I, _I, _I, _P, _P, _P]),
     "kara_token2chunk": (_I, [_I, _I, _I, _I, _P, _P, _P, _P]),
     "kara_paged_compact": (_I, [_P, _P, _I, _P, _I, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "kara_schedule_step": (_I, [ctypes.c_int64, _I, _I, _I, _P, _P, _P, _P, _P]),
 }
 EXPORTED = tuple(_SIGS)
 
@@ -246,3 +247,18 @@ def kara_paged_compact(shape, params, kv_pool, block_table_h, block_table_d, seq
         _host_i32(new_block_table_h, "new_block_table_h"),
         _dev(new_block_table_d, "new_block_table_d", torch.int32),
         _host_i32(new_seq_lens_h, "new_seq_lens_h"), _stream(stream)))
+
+
+def kara_schedule_step(step, period, window, seq_lens, watermarks, selected):
+    """Host-side periodic schedule: returns the list of sequences to compress.
+
+    seq_lens, watermarks: int32 CPU tensors [n_seqs]; selected: uint8/bool CPU
+    tensor [n_seqs] (the caller's random subset)."""
+    n = seq_lens.numel()
+    sel = selected.to(torch.uint8).contiguous()
+    out = torch.empty(max(n, 1), dtype=torch.int32)
+    nb = ctypes.c_int32(0)
+    _check(_lib.kara_schedule_step(int(step), int(period), int(window), n,
+                                   _host_i32(seq_lens, "seq_lens"), _host_i32(watermarks, "watermarks"),
+                                   sel.data_ptr(), out.data_ptr(), ctypes.byref(nb)))
+    return out[:nb.value].tolist()

@@ -88,6 +88,11 @@ CONFIGS = {
     2: dict(name="qwen3-4b-36layer-b32", n_seqs=32, n_layers=36, n_q_heads=32, n_kv_heads=8,
             head_dim=128, block_size=16, window=1024, protect=128, top_k=64, retention=0.2,
             lens=(4096, 16384), dtype=torch.bfloat16, qk_std=128 ** -0.5, planted=4),
+    # one compression event of the Distill-Llama-8B-shaped serving trace, as a
+    # static batch (the trace itself lives in trace.py)
+    4: dict(name="distill-llama-8b-event-b16", n_seqs=16, n_layers=32, n_q_heads=32, n_kv_heads=8,
+            head_dim=128, block_size=16, window=1024, protect=128, top_k=64, retention=0.2,
+            lens=(2048, 13400), dtype=torch.bfloat16, qk_std=128 ** -0.5, planted=4, span_len=(4, 256)),
     3: dict(name="qwen3-14b-40layer-b128", n_seqs=128, n_layers=40, n_q_heads=40, n_kv_heads=8,
             head_dim=128, block_size=16, window=2048, protect=256, top_k=128, retention=0.3,
             lens=(8192, 32768), dtype=torch.bfloat16, qk_std=128 ** -0.5, planted=0,

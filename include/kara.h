@@ -222,6 +222,27 @@ kara_status kara_paged_compact(const kara_shape* shape, const kara_params* param
                                int32_t* new_block_table_h, int32_t* new_block_table_d,
                                int32_t* new_seq_lens_h, void* stream);
 
+/* Periodic compression schedule ("Technical Summary: Kara", Methodology 3,
+ * Periodic Compression Policy: every fixed number of decode steps the
+ * trailing blocks of selected sequences are compressed; Summary, Methodology
+ * intro and Paper, Abstract: compression acts only on recently generated
+ * context).
+ *
+ * At a decode step `step` that is a positive multiple of `period`, a sequence
+ * b is compressed when the caller selected it (selected[b] != 0; the random
+ * draw that picks the subset is the caller's) and its whole trailing window
+ * lies after its watermark: seq_lens[b] - watermarks[b] >= window.  The
+ * watermark is the length below which tokens have already been through a
+ * compressed region; after a compression the caller sets it to
+ * new_len - protect, so the protected tokens are scored again next time and
+ * no token is compressed twice.  A fresh sequence has watermark 0.
+ * Writes the eligible sequence indices, ascending, to batch_out[0..*n_batch)
+ * (batch_out holds n_seqs entries).  At other steps *n_batch = 0.
+ * KARA_E_INVAL on bad arguments (nothing written). */
+kara_status kara_schedule_step(int64_t step, int32_t period, int32_t window, int32_t n_seqs,
+                               const int32_t* seq_lens, const int32_t* watermarks,
+                               const uint8_t* selected, int32_t* batch_out, int32_t* n_batch);
+
 #ifdef __cplusplus
 }
 #endif

@@ -33,4 +33,5 @@ from .kara_oracle import (  # noqa: F401
     window_keys,
     compress,
     logical_tokens,
+    schedule_step,
 )

@@ -307,6 +307,24 @@ def apply_compaction(pool_arr, table, lens, new_table, window, protect, budget,
 
 
 # ----------------------------------------------------------------------------
+# Periodic schedule  [Summary, Methodology 3, Periodic Compression Policy;
+# Summary, Methodology intro: compression only of recently generated context]
+# ----------------------------------------------------------------------------
+
+def schedule_step(step, period, window, lens, watermarks, selected):
+    """Sequences compressed at decode step `step`, ascending.
+
+    Only at positive multiples of the period; among the caller's selected
+    sequences, those whose trailing window holds only tokens that have not yet
+    been through a compressed region (length - watermark >= W).  The caller
+    moves a compressed sequence's watermark to new_length - B.
+    """
+    if step <= 0 or step % period:
+        return []
+    return [b for b in range(len(lens)) if selected[b] and lens[b] - watermarks[b] >= window]
+
+
+# ----------------------------------------------------------------------------
 # End to end
 # ----------------------------------------------------------------------------
 

@@ -169,3 +169,44 @@ def test_stage_entry_points_validate():
     assert kara.lib.kara_token2chunk(4, 10, 3, 11, FAKE, FAKE, FAKE, None) == kara.KARA_E_INVAL
     assert kara.lib.kara_token2chunk(-1, 10, 3, 5, FAKE, FAKE, FAKE, None) == kara.KARA_E_INVAL
     assert kara.lib.kara_topk(0, 10, 3, None, None, None) == kara.KARA_OK     # nothing to do
+
+
+def test_schedule_worked_example():
+    """Step 256 with period 128 and W=1024: seq 0 has 3000 fresh tokens (eligible), seq 1 only
+    500 past its watermark, seq 2 is shorter than the window, seq 3 was not selected."""
+    import torch
+    lens = torch.tensor([3000, 5000, 900, 2048], dtype=torch.int32)
+    wm = torch.tensor([0, 4500, 0, 0], dtype=torch.int32)
+    sel = torch.tensor([1, 1, 1, 0], dtype=torch.uint8)
+    assert kara.kara_schedule_step(256, 128, 1024, lens, wm, sel) == [0]
+    assert kara.kara_schedule_step(200, 128, 1024, lens, wm, sel) == []     # not a period boundary
+    assert kara.kara_schedule_step(0, 128, 1024, lens, wm, sel) == []
+
+
+def test_schedule_matches_oracle():
+    import numpy as np
+    import torch
+
+    from oracle import kara_oracle as ko
+    rng = np.random.default_rng(3)
+    for trial in range(50):
+        n = int(rng.integers(0, 40))
+        lens = rng.integers(1, 5000, size=n)
+        wm = np.array([int(rng.integers(0, L + 1)) for L in lens], dtype=np.int64)
+        sel = rng.random(n) < 0.5
+        step = int(rng.integers(0, 1000))
+        P = int(rng.integers(1, 200))
+        W = int(rng.integers(1, 3000))
+        want = ko.schedule_step(step, P, W, lens.tolist(), wm.tolist(), sel.tolist())
+        got = kara.kara_schedule_step(step, P, W, torch.tensor(lens, dtype=torch.int32),
+                                      torch.tensor(wm, dtype=torch.int32), torch.tensor(sel))
+        assert got == want
+
+
+def test_schedule_rejects():
+    import torch
+    lens = torch.tensor([100], dtype=torch.int32)
+    with pytest.raises(kara.KaraError):
+        kara.kara_schedule_step(128, 128, 10, lens, torch.tensor([101], dtype=torch.int32), torch.tensor([1]))
+    with pytest.raises(kara.KaraError):
+        kara.kara_schedule_step(128, 0, 10, lens, torch.tensor([0], dtype=torch.int32), torch.tensor([1]))
