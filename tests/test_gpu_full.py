@@ -22,11 +22,11 @@ if torch.cuda.is_available():
 def block_checksums(pool):
     """Per-block int64 sum of the 32-bit words of every layer, K and V."""
     Lyr, _, NB = pool.shape[:3]
-    w = pool.view(torch.int32) if pool.dtype == torch.float32 else pool.view(torch.int16).to(torch.int32)
+    w = pool.view(torch.int32) if pool.dtype == torch.float32 else pool.view(torch.int16)
     out = torch.zeros(NB, dtype=torch.int64, device=pool.device)
     for l in range(Lyr):
         for kv in range(2):
-            out += w[l, kv].reshape(NB, -1).to(torch.int64).sum(dim=1)
+            out += w[l, kv].reshape(NB, -1).sum(dim=1, dtype=torch.int64)
     return out
 
 
@@ -104,3 +104,12 @@ def test_full_size_sampled(cfg):
                 assert torch.equal(want.view(torch.int16) if want.dtype == torch.bfloat16 else want,
                                    got.view(torch.int16) if got.dtype == torch.bfloat16 else got)
     print(f"[case] config {cfg} verdicts {verdicts}", flush=True)
+
+
+@pytest.fixture(autouse=True)
+def _release_memory():
+    yield
+    import gc
+    gc.collect()
+    if torch.cuda.is_available():
+        torch.cuda.empty_cache()
