@@ -157,13 +157,19 @@ def run_trace(args, out_base):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 20; for the trace, all events after warmup)")
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=2, choices=[0, 1, 2, 3, 4])
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=36)
+    ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
+                    help="only run a device-to-device copy of this many GiB three times (the reference "
+                         "kernel that scales the HBM byte counters) and print its size")
     args = ap.parse_args()
+    if args.steps is None:
+        args.steps = 0 if args.config == 4 else 20
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures the compression step on one GPU only; --gpus must be 1 "
@@ -178,6 +184,16 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+
+    if args.copy_calibration:
+        n = int(args.copy_calibration * 2**30)
+        src = torch.ones(n // 4, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": n, "launches": 3}), flush=True)
+        return
 
     if args.config == 4:
         base = {"metric": METRIC, "unit": "window tokens/s", "n_gpus": 1, "higher_is_better": True,

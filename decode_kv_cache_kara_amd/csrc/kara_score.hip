@@ -276,26 +276,27 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void score_kernel(ScoreArgs a
   auto row_stats = [&](int tile0, auto masked) {
 #pragma unroll
     for (int qt = 0; qt < kRT; ++qt) {
-      float v[32];
+      // keys past the window (ragged last tile) are masked in place
+      if constexpr (decltype(masked)::value) {
 #pragma unroll
-      for (int e = 0; e < 32; ++e) {
-        const int kt = e >> 4, r = e & 15;
-        v[e] = acc[kt][qt][r];
-        if constexpr (decltype(masked)::value)
-          v[e] = (tile0 + kt * 32 + acc_row(r, lane) < W) ? v[e] : -INFINITY;
+        for (int e = 0; e < 32; ++e) {
+          const int kt = e >> 4, r = e & 15;
+          if (tile0 + kt * 32 + acc_row(r, lane) >= W) acc[kt][qt][r] = -INFINITY;
+        }
       }
+      auto v = [&](int e) -> float { return acc[e >> 4][qt][e & 15]; };
       float mp[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        mp[k] = fmaxf(v[8 * k], v[8 * k + 1]);
+        mp[k] = fmaxf(v(8 * k), v(8 * k + 1));
 #pragma unroll
-        for (int e = 2; e < 8; ++e) mp[k] = fmaxf(mp[k], v[8 * k + e]);
+        for (int e = 2; e < 8; ++e) mp[k] = fmaxf(mp[k], v(8 * k + e));
       }
       const float mx = fmaxf(fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3])), m_run[qt]);
       const float mc = (mx == -INFINITY) ? 0.0f : mx * c;
       float sp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int e = 0; e < 32; ++e) sp[e & 3] += fast_exp2(fmaf(v[e], c, -mc));
+      for (int e = 0; e < 32; ++e) sp[e & 3] += fast_exp2(fmaf(v(e), c, -mc));
       l_run[qt] = l_run[qt] * fast_exp2(m_run[qt] * c - mc) + ((sp[0] + sp[1]) + (sp[2] + sp[3]));
       m_run[qt] = mx;
     }
