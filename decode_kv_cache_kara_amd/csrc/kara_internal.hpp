@@ -11,15 +11,8 @@ constexpr int kMaxWindow = 4096;
 constexpr int kMaxRegion = 2048;
 
 // Rows (query-head x window-position pairs) scored by one workgroup of the
-// score kernel, and 32-row query tiles per wave (1: 16 waves of 32 rows).
-#ifndef KARA_ROWS_PER_CHUNK
-#define KARA_ROWS_PER_CHUNK 512
-#endif
-constexpr int kScoreRowsPerChunk = KARA_ROWS_PER_CHUNK;
-#ifndef KARA_ROW_TILES
-#define KARA_ROW_TILES 1
-#endif
-constexpr int kScoreRowTiles = KARA_ROW_TILES;
+// score kernel (16 waves x 32 rows).
+constexpr int kScoreRowsPerChunk = 512;
 
 struct ScoreArgs {
   const void* q;          // [S][Lyr][W][Hq][D]

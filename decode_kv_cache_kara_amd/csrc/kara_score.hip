@@ -21,17 +21,20 @@
 // buffered, with a 16-byte row pad so the per-lane 16-byte reads do not
 // collide on banks.
 //
-// The exponentials, not the MFMAs, bound this kernel: per logit pass 1 needs a
-// max, an FMA, an exp2 (half-rate on gfx950) and an add, pass 2 an FMA, an
-// exp2 and an add, against 2*D MFMA flops.  So the schedule is built to keep
-// the VALU busy and hide the matrix work under it:
-//   * ping-pong: waves are split in two groups that share every SIMD; in each
-//     barrier-separated phase one group issues MFMAs while the other runs the
-//     exponentials of the tile it multiplied in the previous phase;
-//   * each wave owns kRT x 32 rows so that several waves of each group sit on
-//     every SIMD and the VALU stream of one wave hides the latency of
-//     another's; sums and maxima are split into independent partial chains;
-//   * key tiles are fetched two phases ahead of their LDS store.
+// Per logit, pass 1 needs a max, an FMA, an exp2 and an add and pass 2 an FMA,
+// an exp2 and an add, against 2*D MFMA flops; on gfx950 v_exp_f32 costs about
+// four FMAs, so the VALU work (about 8.5 ms at the Qwen3-4B 36-layer batch of
+// 32) is as large as the MFMA work (about 7.7 ms), and the two overlap only
+// partially on one SIMD (about 30% of the shorter in microbenchmarks).  The
+// schedule therefore aims at a dense instruction stream rather than at hiding
+// one unit under the other:
+//   * each wave owns 32 rows (at most 128 VGPRs, four waves per SIMD) and
+//     software-pipelines over 32-key subtiles: the MFMAs of the next subtile
+//     are issued between the exponentials of the current one (scheduling
+//     groups below), so no wave waits for its own matrix results;
+//   * LDS holds three 64-key tiles (two being multiplied, one being filled),
+//     so there is one barrier per tile; sums and maxima use independent
+//     partial chains.
 //
 // One workgroup scores 512 rows of one unit.  The workgroups of a unit are
 // dispatched back to back onto the same XCD (block ids are interleaved across
@@ -51,10 +54,9 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kRT = kScoreRowTiles;              // 32-row query tiles per wave
-constexpr int kWaves = kScoreRowsPerChunk / (32 * kRT);
+constexpr int kRowsPerWave = 32;                 // one 32-row query tile per wave
+constexpr int kWaves = kScoreRowsPerChunk / kRowsPerWave;
 constexpr int kThreads = kWaves * 64;
-constexpr int kRowsPerWave = 32 * kRT;
 constexpr int kKeyTile = 64;
 
 template <typename T>
@@ -89,17 +91,17 @@ struct Mma<float> {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+
 // Row (M index) of accumulator element r of lane `lane` in a 32x32 MFMA tile.
 __device__ __forceinline__ int acc_row(int r, int lane) {
   return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 }
 
-// With 32-row waves (at most 128 VGPRs) four waves share each SIMD; ask for
-// enough co-resident workgroups to reach that.
-constexpr int kMinBlocks = kRT == 1 ? (16 / kWaves > 0 ? 16 / kWaves : 1) : 1;
+// 16 waves of at most 128 VGPRs: four waves share each SIMD.
+constexpr int kMinWavesPerEU = 4;
 
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads, kMinBlocks) void score_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(kThreads, kMinWavesPerEU) void score_kernel(ScoreArgs a) {
   using M = Mma<T>;
   typedef typename M::Frag Frag;
   constexpr int NK = D / M::kStep;
@@ -109,7 +111,7 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void score_kernel(ScoreArgs a
   constexpr int kTilePieces = kKeyTile * kPiecesPerRow;
   constexpr int kPerThread = (kTilePieces + kThreads - 1) / kThreads;
 
-  __shared__ __attribute__((aligned(16))) char kbuf[2][kKeyTile * kStride];
+  __shared__ __attribute__((aligned(16))) char kbuf[3][kKeyTile * kStride];
   __shared__ float bias_lds[kWaves * kRowsPerWave];
   __shared__ float col_ring[2][kWaves][kKeyTile];
 
@@ -149,6 +151,7 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void score_kernel(ScoreArgs a
 
   // Query fragments of this wave's rows, kept in registers for both passes.
   // Row r is window position r / G, head r % G of the group.
+  constexpr int kRT = 1;
   Frag qf[kRT][NK];
 #pragma unroll
   for (int qt = 0; qt < kRT; ++qt) {
@@ -164,11 +167,10 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void score_kernel(ScoreArgs a
     }
   }
 
-  // Global -> register staging of key tiles, two register sets so that a
-  // tile's loads are in flight for three phases before they are written to
-  // LDS.  Block sizes are powers of two (bs = 1 << bs_shift).
+  // Global -> register staging of key tiles: a tile is fetched one tile ahead
+  // of its LDS store.  Block sizes are powers of two (bs = 1 << bs_shift).
   typedef uint4 Stage[kPerThread];
-  Stage stage0, stage1;
+  Stage stage0;
   const int bs_mask = (1 << a.bs_shift) - 1;
   auto load_tile = [&](Stage& st, int tile0) {
 #pragma unroll
@@ -203,155 +205,118 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void score_kernel(ScoreArgs a
     return *(const Frag*)p;
   };
 
-  // MFMA of the 64-key tile held in LDS buffer `buf` against this wave's
-  // query tiles: acc[kt][qt].  Pass 1 computes S^T (keys on the M axis), pass
-  // 2 computes S (queries on M).
-  f32x16 acc[2][kRT];
-  auto mma_tile = [&](int buf, auto keys_on_m) {
+  // ---- software-pipelined schedule (one 32-row query tile per wave) -------
+  // Within each wave the MFMAs of the next 32-key subtile are issued between
+  // the exponentials of the current one (scheduling groups below), so the
+  // matrix core and the VALU of every SIMD work at the same time.  LDS holds
+  // three key tiles: the two being multiplied and the one being filled.
+  f32x16 accA, accB;
+  auto mma_sub = [&](f32x16& acc, int buf, int kt, auto keys_on_m) {
+    f32x16 z = {};
+    acc = z;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      f32x16 z = {};
-#pragma unroll
-      for (int qt = 0; qt < kRT; ++qt) acc[kt][qt] = z;
-#pragma unroll
-      for (int ks = 0; ks < NK; ++ks) {
-        const Frag kf = kfrag(buf, kt, ks);
-#pragma unroll
-        for (int qt = 0; qt < kRT; ++qt) {
-          if constexpr (decltype(keys_on_m)::value) acc[kt][qt] = M::run(kf, qf[qt][ks], acc[kt][qt]);
-          else acc[kt][qt] = M::run(qf[qt][ks], kf, acc[kt][qt]);
-        }
-      }
+    for (int ks = 0; ks < NK; ++ks) {
+      const Frag kf = kfrag(buf, kt, ks);
+      if constexpr (decltype(keys_on_m)::value) acc = M::run(kf, qf[0][ks], acc);
+      else acc = M::run(qf[0][ks], kf, acc);
     }
   };
-
-  // Ping-pong schedule.  Group A (waves 0..kWaves/2-1) and group B share the
-  // SIMDs evenly (wave w runs on the SIMD of wave w mod 4).  Time runs in
-  // barrier-separated phases, two per key tile; a wave multiplies tile t in
-  // one phase and runs the exponentials of that tile in the next, and group B
-  // runs one phase behind group A:
-  //   phase    2t        2t+1       2t+2
-  //   group A  MFMA(t)   VALU(t)    MFMA(t+1)
-  //   group B  VALU(t-1) MFMA(t)    VALU(t)
-  // Tile t+2 is fetched from global memory in phase 2t and written to LDS in
-  // phase 2t+3.
-#ifndef KARA_PINGPONG
-#define KARA_PINGPONG 1
-#endif
-  const int lag = (KARA_PINGPONG && wave >= kWaves / 2) ? 1 : 0;
-  auto pipeline = [&](int n_tiles, auto work) {
+  auto interleave = [&]() {
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  };
+  // Keeps a step's VALU results ahead of the point that follows (the compiler
+  // would otherwise sink the exponentials past the next barrier, away from the
+  // MFMAs they are meant to overlap).
+  auto pin = [](float x, float y) { asm volatile("" ::"v"(x), "v"(y)); };
+  auto prologue = [&](int n_tiles) {
     load_tile(stage0, 0);
     store_tile(stage0, 0);
-    if (n_tiles > 1) load_tile(stage1, kKeyTile);
+    load_tile(stage0, (n_tiles > 1 ? 1 : 0) * kKeyTile);
+    store_tile(stage0, 1);
     __syncthreads();
-    auto phase_pair = [&](int t, Stage& ld, const Stage& st) {
-      if (t > n_tiles) return;
-      if (t + 2 < n_tiles) load_tile(ld, (t + 2) * kKeyTile);   // same parity as t
-      {
-        const int q = 2 * t - lag;
-        if (q >= 0 && q < 2 * n_tiles) work(q, 2 * t);
-      }
-      __syncthreads();
-      if (t == n_tiles) return;
-      {
-        const int q = 2 * t + 1 - lag;
-        if (q < 2 * n_tiles) work(q, 2 * t + 1);
-      }
-      if (t + 1 < n_tiles) store_tile(st, (t + 1) & 1);         // loaded two phases ago
-      __syncthreads();
-    };
-    for (int t = 0; t <= n_tiles; t += 2) {
-      phase_pair(t, stage0, stage1);
-      phase_pair(t + 1, stage1, stage0);
-    }
+    load_tile(stage0, (n_tiles > 2 ? 2 : n_tiles - 1) * kKeyTile);
   };
 
   // ---------------- pass 1: row max and exp-sum over all W keys -------------
-  float m_run[kRT], l_run[kRT];
+  float m_run = -INFINITY, l_run = 0.0f;
+  auto stats_sub = [&](f32x16& acc, int key0, auto masked) {
+    if constexpr (decltype(masked)::value) {
 #pragma unroll
-  for (int qt = 0; qt < kRT; ++qt) {
-    m_run[qt] = -INFINITY;
-    l_run[qt] = 0.0f;
-  }
-  auto row_stats = [&](int tile0, auto masked) {
-#pragma unroll
-    for (int qt = 0; qt < kRT; ++qt) {
-      // keys past the window (ragged last tile) are masked in place
-      if constexpr (decltype(masked)::value) {
-#pragma unroll
-        for (int e = 0; e < 32; ++e) {
-          const int kt = e >> 4, r = e & 15;
-          if (tile0 + kt * 32 + acc_row(r, lane) >= W) acc[kt][qt][r] = -INFINITY;
-        }
-      }
-      auto v = [&](int e) -> float { return acc[e >> 4][qt][e & 15]; };
-      float mp[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        mp[k] = fmaxf(v(8 * k), v(8 * k + 1));
-#pragma unroll
-        for (int e = 2; e < 8; ++e) mp[k] = fmaxf(mp[k], v(8 * k + e));
-      }
-      const float mx = fmaxf(fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3])), m_run[qt]);
-      const float mc = (mx == -INFINITY) ? 0.0f : mx * c;
-      float sp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int e = 0; e < 32; ++e) sp[e & 3] += fast_exp2(fmaf(v(e), c, -mc));
-      l_run[qt] = l_run[qt] * fast_exp2(m_run[qt] * c - mc) + ((sp[0] + sp[1]) + (sp[2] + sp[3]));
-      m_run[qt] = mx;
+      for (int r = 0; r < 16; ++r)
+        if (key0 + acc_row(r, lane) >= W) acc[r] = -INFINITY;
     }
+    float m0 = fmaxf(acc[0], acc[1]), m1 = fmaxf(acc[8], acc[9]);
+#pragma unroll
+    for (int r = 2; r < 8; ++r) {
+      m0 = fmaxf(m0, acc[r]);
+      m1 = fmaxf(m1, acc[8 + r]);
+    }
+    const float mx = fmaxf(fmaxf(m0, m1), m_run);
+    const float mc = (mx == -INFINITY) ? 0.0f : mx * c;
+    float sp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sp[r & 3] += fast_exp2(fmaf(acc[r], c, -mc));
+    l_run = l_run * fast_exp2(m_run * c - mc) + ((sp[0] + sp[1]) + (sp[2] + sp[3]));
+    m_run = mx;
   };
-
   const int T1 = (W + kKeyTile - 1) / kKeyTile;
-  pipeline(T1, [&](int q, int) {
-    const int tq = q >> 1;
-    if (!(q & 1)) {
-      mma_tile(tq & 1, std::true_type());
-    } else if (tq + 1 < T1) {
-      row_stats(tq * kKeyTile, std::false_type());
-    } else {
-      row_stats(tq * kKeyTile, std::true_type());
-    }
-  });
+  prologue(T1);
+  mma_sub(accA, 0, 0, std::true_type());
+  for (int t = 0; t + 1 < T1; ++t) {
+    const int b0 = t % 3, b1 = (t + 1) % 3, b2 = (t + 2) % 3;
+    mma_sub(accB, b0, 1, std::true_type());
+    stats_sub(accA, t * kKeyTile, std::false_type());
+    interleave();
+    pin(m_run, l_run);
+    mma_sub(accA, b1, 0, std::true_type());
+    stats_sub(accB, t * kKeyTile + 32, std::false_type());
+    interleave();
+    pin(m_run, l_run);
+    store_tile(stage0, b2);
+    __syncthreads();
+    load_tile(stage0, (t + 3 < T1 ? t + 3 : T1 - 1) * kKeyTile);
+  }
+  {
+    const int t = T1 - 1;
+    mma_sub(accB, t % 3, 1, std::true_type());
+    stats_sub(accA, t * kKeyTile, std::true_type());
+    stats_sub(accB, t * kKeyTile + 32, std::true_type());
+  }
+  __syncthreads();
 
   // Merge the two lane halves (same query, disjoint keys) and publish the row
   // bias  m*c + log2(sum)  so that  p = exp2(x*c - bias).
-#pragma unroll
-  for (int qt = 0; qt < kRT; ++qt) {
-    const float mo = __shfl_xor(m_run[qt], 32);
-    const float lo = __shfl_xor(l_run[qt], 32);
-    const float mm = fmaxf(m_run[qt], mo);
+  {
+    const float mo = __shfl_xor(m_run, 32);
+    const float lo = __shfl_xor(l_run, 32);
+    const float mm = fmaxf(m_run, mo);
     const float mc = mm * c;
-    const float sum = l_run[qt] * fast_exp2(m_run[qt] * c - mc) + lo * fast_exp2(mo * c - mc);
-    const int row = row0 + qt * 32 + (lane & 31);
+    const float sum = l_run * fast_exp2(m_run * c - mc) + lo * fast_exp2(mo * c - mc);
+    const int row = row0 + (lane & 31);
     const float bias = (row < rows) ? mc + log2f(sum) : INFINITY;
-    if (lane < 32) bias_lds[wave * kRowsPerWave + qt * 32 + lane] = bias;
+    if (lane < 32) bias_lds[wave * kRowsPerWave + lane] = bias;
   }
   __syncthreads();
 
   // ---------------- pass 2: column sums over keys j < C ---------------------
   const int T2 = (C + kKeyTile - 1) / kKeyTile;
-  float nbias[kRT][16];
+  float nbias[16];
 #pragma unroll
-  for (int qt = 0; qt < kRT; ++qt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) nbias[qt][r] = -bias_lds[wave * kRowsPerWave + qt * 32 + acc_row(r, lane)];
-
-  // Per-wave column sums of a tile go to a two-tile ring in LDS; once both
-  // groups have added theirs, wave 0 sums the waves in order and writes out.
+  for (int r = 0; r < 16; ++r) nbias[r] = -bias_lds[wave * kRowsPerWave + acc_row(r, lane)];
   float* out = a.out + ((size_t)unit * a.n_split + chunk) * C;
-  auto col_sums = [&](int t) {
+  auto col_sub = [&](const f32x16& acc, int t, int kt) {
+    float sp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      float sp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int qt = 0; qt < kRT; ++qt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sp[r & 3] += fast_exp2(fmaf(acc[kt][qt][r], c, nbias[qt][r]));
-      float col = (sp[0] + sp[1]) + (sp[2] + sp[3]);
-      col += __shfl_xor(col, 32);
-      if (lane < 32) col_ring[t & 1][wave][kt * 32 + lane] = col;
-    }
+    for (int r = 0; r < 16; ++r) sp[r & 3] += fast_exp2(fmaf(acc[r], c, nbias[r]));
+    float col = (sp[0] + sp[1]) + (sp[2] + sp[3]);
+    col += __shfl_xor(col, 32);
+    if (lane < 32) col_ring[t & 1][wave][kt * 32 + lane] = col;
   };
   auto flush_cols = [&](int t) {
     const int key = t * kKeyTile + lane;
@@ -362,15 +327,30 @@ __global__ __launch_bounds__(kThreads, kMinBlocks) void score_kernel(ScoreArgs a
       out[key] = sum;
     }
   };
-
-  pipeline(T2, [&](int q, int p) {
-    // tile t's column partials are complete after phase 2t+2; flush them in 2t+3
-    if ((p & 1) && p >= 3) flush_cols((p - 3) >> 1);
-    const int tq = q >> 1;
-    if (!(q & 1)) mma_tile(tq & 1, std::false_type());
-    else col_sums(tq);
-  });
-  flush_cols(T2 - 1);
+  prologue(T2);
+  mma_sub(accA, 0, 0, std::false_type());
+  for (int t = 0; t + 1 < T2; ++t) {
+    const int b0 = t % 3, b1 = (t + 1) % 3, b2 = (t + 2) % 3;
+    if (t > 0) flush_cols(t - 1);
+    mma_sub(accB, b0, 1, std::false_type());
+    col_sub(accA, t, 0);
+    interleave();
+    mma_sub(accA, b1, 0, std::false_type());
+    col_sub(accB, t, 1);
+    interleave();
+    store_tile(stage0, b2);
+    __syncthreads();
+    load_tile(stage0, (t + 3 < T2 ? t + 3 : T2 - 1) * kKeyTile);
+  }
+  {
+    const int t = T2 - 1;
+    if (t > 0) flush_cols(t - 1);
+    mma_sub(accB, t % 3, 1, std::false_type());
+    col_sub(accA, t, 0);
+    col_sub(accB, t, 1);
+    __syncthreads();
+    flush_cols(t);
+  }
 }
 
 __global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ partials,
