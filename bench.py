@@ -56,10 +56,10 @@ def read_traffic(workload):
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(cfg, n_layers_sample, seed):
-    """Oracle compress() on 1 sequence x n_layers_sample layers of the same
-    shapes, extrapolated to the metric's unit (window tokens of the full
-    model slice per second)."""
+def cpu_baseline(cfg, n_layers_sample, seed, n_seqs_sample=3):
+    """Oracle compress() on n_seqs_sample sequences x n_layers_sample layers of
+    the same shapes, extrapolated to the metric's unit (window tokens of the
+    full model slice per second)."""
     import numpy as np
     import torch
     from threadpoolctl import threadpool_info
@@ -68,7 +68,7 @@ def cpu_baseline(cfg, n_layers_sample, seed):
     from oracle import kara_oracle as ko
 
     full = synth.CONFIGS[cfg]
-    wl = synth.make_workload(cfg, seed=seed, device="cpu", n_seqs=1, n_layers=n_layers_sample)
+    wl = synth.make_workload(cfg, seed=seed, device="cpu", n_seqs=n_seqs_sample, n_layers=n_layers_sample)
     q = wl.q_window.to(torch.float64).numpy()
     pool = wl.pool.to(torch.float64).numpy()
     table = wl.table.long().numpy()
@@ -78,12 +78,12 @@ def cpu_baseline(cfg, n_layers_sample, seed):
                 wl.free_ids)
     dt = time.perf_counter() - t0
     frac = n_layers_sample / full["n_layers"]
-    value = wl.window * frac / dt
+    value = n_seqs_sample * wl.window * frac / dt
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     return {"value": value, "unit": "window tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": (f"oracle compress() (fp64 scores, Top-K, Token2Chunk, pool plan, row gather) on 1 "
-                       f"sequence x {n_layers_sample} of {full['n_layers']} layers of the same shapes "
-                       f"(L={int(lens[0])}), {dt:.1f} s, scaled to the full layer count")}
+            "sample": (f"oracle compress() (fp64 scores, Top-K, Token2Chunk, pool plan, row gather) on "
+                       f"{n_seqs_sample} sequences x {n_layers_sample} of {full['n_layers']} layers of the same "
+                       f"shapes (L={[int(x) for x in lens]}), {dt:.1f} s, scaled to the full layer count")}
 
 
 def run_trace(args, out_base):
