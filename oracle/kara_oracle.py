@@ -41,9 +41,18 @@ repository's design notes):
     old blocks from the boundary block to the old end are pushed to the back
     of the list after all fresh blocks are taken.
 
-The chunk-score formula is this build's own (the pages leave it open), so the
+The chunk-score formula is this library's own reading (the pages leave it open), so the
 Token2Chunk result is pinned against that stated formula only; parity with
 the paper's unpublished formula is unpinned.
+
+Ablations [Summary, Experimental Results, Ablation Studies: removing the
+bidirectional scoring or the Token2Chunk module each costs accuracy]:
+
+  * unidirectional scoring: window query i takes its softmax over window keys
+    j <= i only (the causal attention the model itself computes), so key j
+    is scored by the queries at and after it; everything else is unchanged;
+  * Token2Chunk off: the kept set is the top-R set of the region (isolated
+    pairs, ties to the lower index), i.e. the candidates are never expanded.
 """
 
 from __future__ import annotations
@@ -58,12 +67,13 @@ import numpy as np
 # Scoring  [Summary, Methodology 1, Mechanism / Rationale]
 # ----------------------------------------------------------------------------
 
-def window_scores(q_win, k_win, protect):
+def window_scores(q_win, k_win, protect, unidirectional=False):
     """Bidirectional window attention scores of the compressible region.
 
     q_win: [W, Hq, D] window query states (any float dtype; upcast to float64).
     k_win: [W, Hkv, D] window key states.
     protect: B, the length of the protected buffer at the end of the window.
+    unidirectional: the ablation; row i's softmax runs over keys j <= i only.
     Returns s: float64 [Hkv, C] with C = W - B.
 
     For every KV head h and every query head q of its group (q // G == h), every
@@ -90,9 +100,11 @@ def window_scores(q_win, k_win, protect):
         for g in range(G):
             queries = q[:, h * G + g, :]           # [W, D]
             logits = (queries @ keys.T) * scale    # row i: query i, column j: key j
+            if unidirectional:                     # keys after the query are not seen
+                logits = np.where(np.tril(np.ones((W, W), dtype=bool)), logits, -np.inf)
             logits = logits - logits.max(axis=1, keepdims=True)
             e = np.exp(logits)
-            p = e / e.sum(axis=1, keepdims=True)   # row softmax over all W keys
+            p = e / e.sum(axis=1, keepdims=True)   # row softmax over the keys it sees
             s[h] += p[:, :C].sum(axis=0)           # accumulate per key j < C
     return s
 
@@ -183,8 +195,11 @@ def token2chunk(scores, cand, budget, return_spans=False):
     return (out, accepted) if return_spans else out
 
 
-def select_retained(scores, top_k, budget):
-    """Top-K then Token2Chunk on one unit's region scores."""
+def select_retained(scores, top_k, budget, chunks=True):
+    """Top-K then Token2Chunk on one unit's region scores; with chunks=False
+    (the ablation) the kept set is the top-R set."""
+    if not chunks:
+        return topk_candidates(scores, budget)
     cand = topk_candidates(scores, top_k)
     return token2chunk(scores, cand, budget)
 
@@ -329,7 +344,7 @@ def schedule_step(step, period, window, lens, watermarks, selected):
 # ----------------------------------------------------------------------------
 
 def compress(q_window, pool_arr, table, lens, window, protect, top_k, budget,
-             block_size, free_ids, units=None):
+             block_size, free_ids, units=None, unidirectional=False, chunks=True):
     """Whole step on host arrays.
 
     q_window: [S, Lyr, W, Hq, D]; pool_arr: [Lyr, 2, NB, Hkv, bs, D].
@@ -337,6 +352,7 @@ def compress(q_window, pool_arr, table, lens, window, protect, top_k, budget,
     units:    optional iterable of (b, l) pairs to score; other pairs are left
               unscored (used to sample large workloads).  Compaction needs
               every unit, so it runs only when ``units`` is None.
+    unidirectional, chunks: the ablations (see the module header).
     Returns a dict with scores [S, Lyr, Hkv, C], cand [S, Lyr, Hkv, K],
     retained [S, Lyr, Hkv, R] (rows not scored hold -1), and when compacted:
     pool, table, lens, free_ids.
@@ -352,12 +368,12 @@ def compress(q_window, pool_arr, table, lens, window, protect, top_k, budget,
     todo = [(b, l) for b in range(S) for l in range(Lyr)] if units is None else list(units)
     for b, l in todo:
         k_win = window_keys(pool_arr, table[b], int(lens[b]), window, l, Hkv, block_size)
-        s = window_scores(q_window[b, l], k_win, protect)
+        s = window_scores(q_window[b, l], k_win, protect, unidirectional)
         scores[b, l] = s
         for h in range(Hkv):
             c = topk_candidates(s[h], top_k)
             cand[b, l, h] = c
-            retained[b, l, h] = token2chunk(s[h], c, budget)
+            retained[b, l, h] = token2chunk(s[h], c, budget) if chunks else topk_candidates(s[h], budget)
     out = dict(scores=scores, cand=cand, retained=retained)
     if units is None:
         pool = FifoPool(free_ids)
