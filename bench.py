@@ -56,7 +56,7 @@ def read_traffic(workload):
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(cfg, n_layers_sample, seed, n_seqs_sample=3):
+def cpu_baseline(cfg, n_layers_sample, seed, n_seqs_sample=3, flags=0):
     """Oracle compress() on n_seqs_sample sequences x n_layers_sample layers of
     the same shapes, extrapolated to the metric's unit (window tokens of the
     full model slice per second)."""
@@ -75,7 +75,7 @@ def cpu_baseline(cfg, n_layers_sample, seed, n_seqs_sample=3):
     lens = wl.lens.long().numpy()
     t0 = time.perf_counter()
     ko.compress(q, pool, table, lens, wl.window, wl.protect, wl.top_k, wl.budget, wl.block_size,
-                wl.free_ids)
+                wl.free_ids, unidirectional=bool(flags & 1), chunks=not (flags & 2))
     dt = time.perf_counter() - t0
     frac = n_layers_sample / full["n_layers"]
     value = n_seqs_sample * wl.window * frac / dt
@@ -162,6 +162,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=2, choices=[0, 1, 2, 3, 4])
     ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--flags", type=int, default=0, choices=[0, 1, 2, 3],
+                    help="ablations: 1 unidirectional scoring, 2 Token2Chunk off, 3 both")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=36)
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
@@ -210,7 +212,7 @@ def main():
     torch.cuda.synchronize()
     log(f"workload {wl.name}: {wl.n_seqs} seqs x {wl.n_layers} layers, pool {wl.n_blocks} blocks "
         f"({wl.pool.numel() * wl.pool.element_size() / 2**30:.1f} GiB), generated in {time.time() - t0:.1f} s")
-    ses = runner.Session(wl, outputs=False)
+    ses = runner.Session(wl, outputs=False, flags=args.flags)
     stream = torch.cuda.current_stream()
 
     def events():
@@ -249,7 +251,10 @@ def main():
     elt = wl.pool.element_size()
     tokens = S * W
     value = tokens / (ms_per_step / 1e3)
-    score_flop = 2.0 * S * Lyr * Hq * W * W * D
+    uni = bool(args.flags & kara.UNIDIRECTIONAL)
+    # one QK^T over the window: all W x W logits, or (unidirectional) the
+    # W (W + 1) / 2 that causal attention needs
+    score_flop = 2.0 * S * Lyr * Hq * (W * (W + 1) / 2 if uni else W * W) * D
     exec_flop = 2.0 * S * Lyr * Hq * W * (math.ceil(W / 64) * 64 + math.ceil(C / 64) * 64) * D
     score_tflops = score_flop / (stage[0] / 1e3) / 1e12
     peak = PEAK_BF16_TFLOPS if wl.dtype == torch.bfloat16 else PEAK_FP32_MFMA_TFLOPS
@@ -257,7 +262,7 @@ def main():
     rows = sum(((L - W) % wl.block_size) + wl.budget + wl.protect for L in lens)
     compact_bytes = 2.0 * rows * Lyr * 2 * Hkv * D * elt
     compact_gbs = compact_bytes / (stage[2] / 1e3) / 1e9
-    traffic = read_traffic(wl.name)
+    traffic = read_traffic(wl.name) if args.flags == 0 else None
 
     out = {
         "metric": METRIC,
@@ -275,11 +280,12 @@ def main():
         "config": {"workload": wl.name, "n_seqs": S, "n_layers": Lyr, "n_q_heads": Hq, "n_kv_heads": Hkv,
                    "head_dim": D, "window": W, "protect": wl.protect, "top_k": wl.top_k,
                    "budget": wl.budget, "block_size": wl.block_size,
-                   "seq_lens": f"U[{min(lens)}..{max(lens)}] seed {wl.seed}"},
+                   "seq_lens": f"U[{min(lens)}..{max(lens)}] seed {wl.seed}",
+                   "ablation": {0: "none", 1: "unidirectional", 2: "no_chunks", 3: "unidirectional+no_chunks"}[args.flags]},
         "roofline": {"bound": "mfma", "kernel": "score_kernel", "achieved": round(score_tflops, 2),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(score_tflops / peak, 4),
                      "traffic": traffic, "algorithmic_flop_per_launch": score_flop,
-                     "executed_mfma_flop_per_launch": exec_flop},
+                     "executed_mfma_flop_per_launch": exec_flop if not uni else None},
         "stages_ms": {"score": round(stage[0], 4), "select": round(stage[1], 4),
                       "compact": round(stage[2], 4)},
         "compact_roofline": {"bound": "hbm", "kernel": "compact_kernel", "achieved": round(compact_gbs, 1),
@@ -291,7 +297,7 @@ def main():
         torch.cuda.empty_cache()
         log("timing the CPU oracle on a sample ...")
         n_layers_sample = min(args.cpu_layers, synth.CONFIGS[args.config]["n_layers"])
-        out["cpu_baseline"] = cpu_baseline(args.config, n_layers_sample, seed=7)
+        out["cpu_baseline"] = cpu_baseline(args.config, n_layers_sample, seed=7, flags=args.flags)
         log(f"cpu baseline {out['cpu_baseline']['value']:.1f} window tokens/s")
     print(json.dumps(out), flush=True)
 

@@ -77,6 +77,8 @@ kara_status check_params(const kara_params* p) {
     return fail(KARA_E_INVAL, "compressible region %d exceeds %d", C, kara::kMaxRegion);
   if (p->top_k < 1 || p->top_k > C) return fail(KARA_E_INVAL, "top_k %d outside [1, %d]", p->top_k, C);
   if (p->budget < 1 || p->budget > C) return fail(KARA_E_INVAL, "budget %d outside [1, %d]", p->budget, C);
+  if (p->flags & ~(KARA_UNIDIRECTIONAL | KARA_NO_CHUNKS))
+    return fail(KARA_E_INVAL, "flags 0x%x hold unknown bits", (unsigned)p->flags);
   return KARA_OK;
 }
 
@@ -208,6 +210,7 @@ kara::ScoreArgs score_args(const kara_shape* sh, const kara_params* p, int32_t n
   a.n_split = kara::score_chunks(a.G, a.W);
   a.n_units = n_seqs * sh->n_layers * sh->n_kv_heads;
   a.c = (float)(1.4426950408889634 / std::sqrt((double)sh->head_dim));
+  a.unidirectional = (p->flags & KARA_UNIDIRECTIONAL) ? 1 : 0;
   return a;
 }
 
@@ -369,6 +372,7 @@ kara_status kara_compress(const kara_shape* shape, const kara_params* params, in
   se.K = params->top_k;
   se.R = params->budget;
   se.mode = kara::kSelectFull;
+  se.no_chunks = (params->flags & KARA_NO_CHUNKS) ? 1 : 0;
   if ((e = kara::launch_select(se, s)) != hipSuccess) return hip_fail(e, "select launch");
   if ((e = mark(2)) != hipSuccess) return hip_fail(e, "stage event");
   kara::CompactArgs ca = compact_args(shape, params, n_seqs, kv_pool, n_blocks, block_table_d,
@@ -429,6 +433,7 @@ kara_status kara_topk(int32_t n_units, int32_t region, int32_t top_k, const floa
   se.K = top_k;
   se.R = top_k;
   se.mode = kara::kSelectTopK;
+  se.no_chunks = 0;
   hipError_t e = kara::launch_select(se, (hipStream_t)stream);
   return e == hipSuccess ? KARA_OK : hip_fail(e, "topk launch");
 }
@@ -454,6 +459,7 @@ kara_status kara_token2chunk(int32_t n_units, int32_t region, int32_t top_k, int
   se.K = top_k;
   se.R = budget;
   se.mode = kara::kSelectT2C;
+  se.no_chunks = 0;
   hipError_t e = kara::launch_select(se, (hipStream_t)stream);
   return e == hipSuccess ? KARA_OK : hip_fail(e, "token2chunk launch");
 }

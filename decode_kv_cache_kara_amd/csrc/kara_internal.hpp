@@ -24,6 +24,7 @@ struct ScoreArgs {
   int n_split;            // row chunks per unit = ceil(G*W / kScoreRowsPerChunk)
   int n_units;            // S * Lyr * Hkv
   float c;                // log2(e) / sqrt(D)
+  int unidirectional;     // 1: query i sees window keys j <= i only
 };
 
 inline int score_chunks(int G, int W) {
@@ -47,6 +48,7 @@ struct SelectArgs {
   int32_t* retained_out;  // [U][R] (kSelectT2C / kSelectFull)
   int n_units, C, K, R;
   int mode;
+  int no_chunks;          // 1: the kept set is the top-R set (no Token2Chunk)
 };
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream);

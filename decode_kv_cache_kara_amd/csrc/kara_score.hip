@@ -36,6 +36,12 @@
 //     so there is one barrier per tile; sums and maxima use independent
 //     partial chains.
 //
+// Unidirectional ablation ("Technical Summary: Kara", Experimental Results,
+// Ablation Studies): window query i sees keys j <= i only.  A workgroup then
+// stops at the key tile that holds its last row's position, subtiles that
+// cross a wave's diagonal are masked element by element, and the partial
+// column sums of keys past the last tile are written as zeros.
+//
 // One workgroup scores 512 rows of one unit.  The workgroups of a unit are
 // dispatched back to back onto the same XCD (block ids are interleaved across
 // the 8 XCDs) so that unit's K rows are fetched from HBM once and then served
@@ -100,7 +106,7 @@ __device__ __forceinline__ int acc_row(int r, int lane) {
 // 16 waves of at most 128 VGPRs: four waves share each SIMD.
 constexpr int kMinWavesPerEU = 4;
 
-template <typename T, int D>
+template <typename T, int D, bool kUni>
 __global__ __launch_bounds__(kThreads, kMinWavesPerEU) void score_kernel(ScoreArgs a) {
   using M = Mma<T>;
   typedef typename M::Frag Frag;
@@ -245,8 +251,20 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerEU) void score_kernel(ScoreAr
 
   // ---------------- pass 1: row max and exp-sum over all W keys -------------
   float m_run = -INFINITY, l_run = 0.0f;
+  // Unidirectional: this lane's query position, and the first position of
+  // the wave (subtiles whose last key is past it cross the diagonal).
+  const int i_lane = (row0 + (lane & 31)) / G;
+  const int i_wave = row0 / G;
   auto stats_sub = [&](f32x16& acc, int key0, auto masked) {
-    if constexpr (decltype(masked)::value) {
+    if constexpr (kUni) {
+      if (key0 + 31 > i_wave) {
+        // key = key0 + acc_row(r, lane) is seen iff key <= i_lane
+        const int lim = i_lane - key0 - 4 * (lane >> 5);
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (8 * (r >> 2) + (r & 3) > lim) acc[r] = -INFINITY;
+      }
+    } else if constexpr (decltype(masked)::value) {
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         if (key0 + acc_row(r, lane) >= W) acc[r] = -INFINITY;
@@ -265,7 +283,16 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerEU) void score_kernel(ScoreAr
     l_run = l_run * fast_exp2(m_run * c - mc) + ((sp[0] + sp[1]) + (sp[2] + sp[3]));
     m_run = mx;
   };
-  const int T1 = (W + kKeyTile - 1) / kKeyTile;
+  // Key tiles: all of the window, or (unidirectional) up to the tile holding
+  // the position of the workgroup's last row.  Uniform over the workgroup.
+  int T1 = (W + kKeyTile - 1) / kKeyTile;
+  int T2 = (C + kKeyTile - 1) / kKeyTile;
+  if constexpr (kUni) {
+    const int last_row = min(rows, (chunk + 1) * kScoreRowsPerChunk) - 1;
+    const int i_last = last_row / G;
+    T1 = i_last / kKeyTile + 1;
+    T2 = min(C - 1, i_last) / kKeyTile + 1;
+  }
   prologue(T1);
   mma_sub(accA, 0, 0, std::true_type());
   for (int t = 0; t + 1 < T1; ++t) {
@@ -305,15 +332,30 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerEU) void score_kernel(ScoreAr
   __syncthreads();
 
   // ---------------- pass 2: column sums over keys j < C ---------------------
-  const int T2 = (C + kKeyTile - 1) / kKeyTile;
   float nbias[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) nbias[r] = -bias_lds[wave * kRowsPerWave + acc_row(r, lane)];
   float* out = a.out + ((size_t)unit * a.n_split + chunk) * C;
   auto col_sub = [&](const f32x16& acc, int t, int kt) {
     float sp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    bool plain = true;
+    if constexpr (kUni) {
+      const int key0 = t * kKeyTile + kt * 32;
+      if (key0 + 31 > i_wave) {
+        // row = row0 + acc_row(r, lane) sees key = key0 + lane%32 iff key*G <= row
+        plain = false;
+        const int lim = (key0 + (lane & 31)) * G - row0 - 4 * (lane >> 5);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sp[r & 3] += fast_exp2(fmaf(acc[r], c, nbias[r]));
+        for (int r = 0; r < 16; ++r) {
+          const float e = fast_exp2(fmaf(acc[r], c, nbias[r]));
+          sp[r & 3] += (8 * (r >> 2) + (r & 3) >= lim) ? e : 0.0f;
+        }
+      }
+    }
+    if (plain) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sp[r & 3] += fast_exp2(fmaf(acc[r], c, nbias[r]));
+    }
     float col = (sp[0] + sp[1]) + (sp[2] + sp[3]);
     col += __shfl_xor(col, 32);
     if (lane < 32) col_ring[t & 1][wave][kt * 32 + lane] = col;
@@ -351,6 +393,10 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerEU) void score_kernel(ScoreAr
     __syncthreads();
     flush_cols(t);
   }
+  if constexpr (kUni) {
+    // keys past the last tile get nothing from this chunk's rows
+    for (int key = T2 * kKeyTile + tid; key < C; key += kThreads) out[key] = 0.0f;
+  }
 }
 
 __global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ partials,
@@ -371,7 +417,10 @@ template <typename T, int D>
 hipError_t launch_typed(const ScoreArgs& a, hipStream_t stream) {
   const int units_pad = (a.n_units + 7) / 8 * 8;
   const unsigned grid = (unsigned)units_pad * (unsigned)a.n_split;
-  hipLaunchKernelGGL((score_kernel<T, D>), dim3(grid), dim3(kThreads), 0, stream, a);
+  if (a.unidirectional)
+    hipLaunchKernelGGL((score_kernel<T, D, true>), dim3(grid), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((score_kernel<T, D, false>), dim3(grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -18,6 +18,9 @@
 // set up to exactly R.  All decisions are integer or exactly specified float32
 // operations, so this kernel and the CPU checker agree bit for bit on the same
 // float32 scores.
+//
+// With Token2Chunk switched off (the ablation of "Technical Summary: Kara",
+// Experimental Results, Ablation Studies) the kept set is the top-R set.
 
 #include "kara_internal.hpp"
 
@@ -313,6 +316,10 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelectArgs a) {
   if (R < K) {
     clear_state(sh, C);
     select_largest(sh, C, R, kCand);
+  } else if (a.no_chunks) {
+    // Token2Chunk off: the top-R set is the top-K set plus the R - K best of
+    // the rest (one total order: score desc, position asc).
+    if (R > K) select_largest(sh, C, R - K, kTopUp);
   } else {
     token2chunk(sh, C, R);
   }

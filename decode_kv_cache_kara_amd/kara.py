@@ -45,7 +45,13 @@ class kara_shape(ctypes.Structure):
 
 class kara_params(ctypes.Structure):
     _fields_ = [("window", ctypes.c_int32), ("protect", ctypes.c_int32),
-                ("top_k", ctypes.c_int32), ("budget", ctypes.c_int32)]
+                ("top_k", ctypes.c_int32), ("budget", ctypes.c_int32),
+                ("flags", ctypes.c_int32)]
+
+
+# kara_params.flags: the two ablations (0 = the method itself)
+UNIDIRECTIONAL = 1
+NO_CHUNKS = 2
 
 
 _P = ctypes.c_void_p

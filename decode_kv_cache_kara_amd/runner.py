@@ -14,8 +14,8 @@ def shape_of(wl):
                            kara.dtype_code(wl.dtype))
 
 
-def params_of(wl):
-    return kara.kara_params(wl.window, wl.protect, wl.top_k, wl.budget)
+def params_of(wl, flags=0):
+    return kara.kara_params(wl.window, wl.protect, wl.top_k, wl.budget, flags)
 
 
 class Session:
@@ -25,12 +25,12 @@ class Session:
     the workload's free list, so repeated calls do identical work.
     """
 
-    def __init__(self, wl, outputs=True):
+    def __init__(self, wl, outputs=True, flags=0):
         if wl.pool.device.type != "cuda":
             raise ValueError("workload must be on the GPU")
         self.wl = wl
         self.shape = shape_of(wl)
-        self.params = params_of(wl)
+        self.params = params_of(wl, flags)
         dev = wl.pool.device
         self.table_h = wl.table.to("cpu", torch.int32).contiguous()
         self.table_d = wl.table.to(torch.int32).contiguous()

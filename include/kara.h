@@ -90,14 +90,29 @@ typedef struct {
   int32_t dtype;           /* kara_dtype */
 } kara_shape;
 
-/* Method parameters: window W, protected buffer B, candidates K, budget R.
- * Valid: 1 <= W <= 4096, 0 <= B < W, C = W - B <= 2048, 1 <= K <= C,
- * 1 <= R <= C. */
+/* Ablation flags for kara_params.flags ("Technical Summary: Kara",
+ * Experimental Results, Ablation Studies: the bidirectional scoring and the
+ * Token2Chunk module are each removed in turn).  0 is the method itself. */
+enum {
+  /* Unidirectional scoring: window query i takes its softmax over window keys
+   * j <= i only (causal attention), so key j is scored by the queries at and
+   * after it. */
+  KARA_UNIDIRECTIONAL = 1,
+  /* Token2Chunk off: the kept set is the top-R set of the region (ties to the
+   * lower position); candidates are never expanded into chunks. */
+  KARA_NO_CHUNKS = 2
+};
+
+/* Method parameters: window W, protected buffer B, candidates K, budget R,
+ * ablation flags.  Valid: 1 <= W <= 4096, 0 <= B < W, C = W - B <= 2048,
+ * 1 <= K <= C, 1 <= R <= C, flags a combination of the KARA_UNIDIRECTIONAL
+ * and KARA_NO_CHUNKS bits. */
 typedef struct {
   int32_t window;
   int32_t protect;
   int32_t top_k;
   int32_t budget;
+  int32_t flags;
 } kara_params;
 
 /* Host free list of block ids: allocation pops the front, freeing pushes the
@@ -166,6 +181,9 @@ size_t kara_workspace_bytes(const kara_shape* shape, const kara_params* params, 
  * stream               hipStream_t.
  * scores_out_d, cand_out_d, retained_out_d   optional dev outputs (NULL: not
  *                      written) in the layouts above.
+ * params->flags        ablations: KARA_UNIDIRECTIONAL scores with causal
+ *                      window attention, KARA_NO_CHUNKS keeps the top-R set
+ *                      (the candidates in cand_out_d are still the top-K).
  * stage_events         optional (NULL: none) array of 4 hipEvent_t, recorded
  *                      on `stream` before the scoring kernel, after it, after
  *                      the selection kernel and after the compaction kernel,
@@ -184,15 +202,17 @@ kara_status kara_compress(const kara_shape* shape, const kara_params* params, in
 
 /* Stage 1 alone: window scores of every unit into scores_d (dev, [n_seqs]
  * [n_layers][n_kv_heads][C] float32).  Arguments as for kara_compress;
- * top_k and budget are validated but unused.  Summary, Methodology 1
- * (Mechanism, Rationale). */
+ * top_k and budget are validated but unused; the KARA_UNIDIRECTIONAL flag
+ * selects the unidirectional ablation.  Summary, Methodology 1 (Mechanism,
+ * Rationale). */
 kara_status kara_score(const kara_shape* shape, const kara_params* params, int32_t n_seqs,
                        const void* q_window, const void* kv_pool, int32_t n_blocks,
                        const int32_t* block_table_h, const int32_t* block_table_d,
                        int32_t max_blocks, const int32_t* seq_lens_h, const int32_t* seq_lens_d,
                        float* scores_d, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Stage 2 alone: for each of n_units rows of `region` float32 scores (dev,
+/* Stage 2 alone (with top_k = R it is also the whole selection of the
+ * KARA_NO_CHUNKS ablation): for each of n_units rows of `region` float32 scores (dev,
  * finite), the top_k positions with the largest score (ties to the lower
  * position, -0 equal to +0), ascending, into cand_d (dev [n_units][top_k]).
  * Summary, Methodology 1 (Selection).  1 <= top_k <= region <= 2048. */

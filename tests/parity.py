@@ -27,14 +27,14 @@ def host_inputs(wl):
     return q, pool, table, lens
 
 
-def oracle_scores(wl, units=None):
+def oracle_scores(wl, units=None, unidirectional=False):
     """float64 scores [S, Lyr, Hkv, C] (rows outside `units` stay NaN)."""
     q, pool, table, lens = host_inputs(wl)
     out = np.full((wl.n_seqs, wl.n_layers, wl.n_kv_heads, wl.region), np.nan)
     todo = units if units is not None else [(b, l) for b in range(wl.n_seqs) for l in range(wl.n_layers)]
     for b, l in todo:
         k = ko.window_keys(pool, table[b], int(lens[b]), wl.window, l, wl.n_kv_heads, wl.block_size)
-        out[b, l] = ko.window_scores(q[b, l], k, wl.protect)
+        out[b, l] = ko.window_scores(q[b, l], k, wl.protect, unidirectional)
     return out
 
 
@@ -55,9 +55,10 @@ def _close(a, b, tol):
     return abs(a - b) <= tol * max(abs(a), abs(b))
 
 
-def adjudicate(s, K, R, X, candX, tol=2 * SCORE_RTOL):
+def adjudicate(s, K, R, X, candX, tol=2 * SCORE_RTOL, chunks=True):
     """Classify the GPU's kept set X and candidates candX of one unit against the
     oracle's float64 scores s: 'exact', 'near_tie' or 'fail: reason'.
+    chunks=False judges the Token2Chunk-off ablation (X must be a top-R set).
 
     'exact' means both equal the oracle's own result.  'near_tie' means they
     differ from it but are a valid result of the method under some perturbation
@@ -71,7 +72,7 @@ def adjudicate(s, K, R, X, candX, tol=2 * SCORE_RTOL):
     X = [int(x) for x in X]
     candX = [int(x) for x in candX]
     candY = ko.topk_candidates(s, K).tolist()
-    Y = ko.token2chunk(s, candY, R).tolist()
+    Y = ko.select_retained(s, K, R, chunks=chunks).tolist()
     if len(X) != R or any(a >= b for a, b in zip(X, X[1:])) or X[0] < 0 or X[-1] >= C:
         return "fail: kept set malformed"
     if len(candX) != K or any(a >= b for a, b in zip(candX, candX[1:])) or candX[0] < 0 or candX[-1] >= C:
@@ -91,7 +92,9 @@ def adjudicate(s, K, R, X, candX, tol=2 * SCORE_RTOL):
     if not best_of_rest_ok(cx, range(C)):
         return "fail: candidates are not a top-K"
     Xs = set(X)
-    if R < K:
+    if R < K or not chunks:
+        if R >= K and not cx <= Xs:
+            return "fail: candidates not kept"
         return "near_tie" if best_of_rest_ok(Xs, range(C)) else "fail: not a top-R set"
     if not cx <= Xs:
         return "fail: candidates not kept"

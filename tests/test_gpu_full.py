@@ -4,7 +4,9 @@ times: Qwen3-4B 36-layer batch 32 (all blocks materialised), Qwen3-14B
 the Distill-Llama-8B-shaped trace as a static batch.  The oracle checks
 sampled (sequence, layer) pairs one by one on the exact bytes the kernels read;
 bookkeeping (tables, lengths, free list) is checked for every sequence, and
-per-block checksums show that no block other than the fresh ones changed."""
+per-block checksums show that no block other than the fresh ones changed.
+The Qwen3-4B batch also runs with both ablations switched on (unidirectional
+scoring, Token2Chunk off)."""
 
 import numpy as np
 import pytest
@@ -36,12 +38,13 @@ def gather_rows(pool, table_row, tokens, l, kv, bs):
     return pool[l, kv, blk, :, t % bs, :]          # [n, Hkv, D]
 
 
-@pytest.mark.parametrize("cfg", [2, 3, 4])
-def test_full_size_sampled(cfg):
-    print(f"[case] full size config {cfg}", flush=True)
+@pytest.mark.parametrize("cfg,flags", [(2, 0), (3, 0), (4, 0), (2, 3)])
+def test_full_size_sampled(cfg, flags):
+    print(f"[case] full size config {cfg} flags {flags}", flush=True)
+    uni, chunks = bool(flags & 1), not (flags & 2)
     wl = synth.make_workload(cfg, device="cuda")
     torch.cuda.synchronize()
-    ses = runner.Session(wl)
+    ses = runner.Session(wl, flags=flags)
     S, Lyr, W, B, bs = wl.n_seqs, wl.n_layers, wl.window, wl.protect, wl.block_size
     rng = np.random.default_rng(cfg)
     samples = sorted({(0, 0), (S - 1, Lyr - 1), (int(rng.integers(S)), int(rng.integers(Lyr)))})
@@ -79,12 +82,12 @@ def test_full_size_sampled(cfg):
     kept = ses.retained.view(S, Lyr, wl.n_kv_heads, -1)
     verdicts = {}
     for b, l in samples:
-        s = ko.window_scores(snap[b, l]["q"], snap[b, l]["k"], B)
+        s = ko.window_scores(snap[b, l]["q"], snap[b, l]["k"], B, unidirectional=uni)
         assert_scores_close(scores[b, l].cpu().numpy(), s, what=f"scores of ({b},{l})")
         kb = kept[b, l].cpu().numpy()
         cb = cand[b, l].cpu().numpy()
         for h in range(wl.n_kv_heads):
-            v = adjudicate(s[h], wl.top_k, wl.budget, kb[h], cb[h])
+            v = adjudicate(s[h], wl.top_k, wl.budget, kb[h], cb[h], chunks=chunks)
             assert not v.startswith("fail"), (b, l, h, v)
             verdicts[v] = verdicts.get(v, 0) + 1
         # compacted rows: the boundary block's leading tokens, the kept tokens, the protected tokens

@@ -80,6 +80,10 @@ def test_workspace_bytes():
     assert 0 < n1 < n4
     assert kara.kara_workspace_bytes(sh, params(window=0), 1) == 0
     assert kara.kara_workspace_bytes(shape(head_dim=96), pr, 1) == 0
+    # the ablation flags do not change the workspace
+    for f in (kara.UNIDIRECTIONAL, kara.NO_CHUNKS, kara.UNIDIRECTIONAL | kara.NO_CHUNKS):
+        assert kara.kara_workspace_bytes(sh, params(flags=f), 4) == n4
+    assert kara.kara_workspace_bytes(sh, params(flags=8), 4) == 0
 
 
 def _i32(vals):
@@ -129,6 +133,8 @@ class Call:
     (dict(params=params(top_k=7)), kara.KARA_E_INVAL),              # K > C
     (dict(params=params(budget=0)), kara.KARA_E_INVAL),             # R < 1
     (dict(params=params(window=5000)), kara.KARA_E_INVAL),
+    (dict(params=params(flags=4)), kara.KARA_E_INVAL),              # unknown ablation bit
+    (dict(params=params(flags=-1)), kara.KARA_E_INVAL),
     (dict(shape=shape(head_dim=96)), kara.KARA_E_UNSUPPORTED),
     (dict(shape=shape(dtype=7)), kara.KARA_E_UNSUPPORTED),
     (dict(shape=shape(n_q_heads=7)), kara.KARA_E_INVAL),

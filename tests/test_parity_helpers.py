@@ -43,3 +43,18 @@ def test_adjudicator_accepts_near_tie():
     cand = [4, 7, 13, 15]
     X = ko.token2chunk(s, np.array(cand), 4)
     assert adjudicate(s, 4, 4, X, cand) == "near_tie"
+
+
+def test_adjudicator_no_chunks():
+    """Token2Chunk-off ablation: the kept set must be a top-R set."""
+    s = np.array([1.0, 5.0, 2.0, 2.0, 7.0, 1.0, 0.5, 6.0, 3.0, 3.0, 0.25, 0.25, 4.0, 8.0, 1.5, 5.0])
+    cand = [1, 4, 7, 13]
+    top9 = [1, 2, 4, 7, 8, 9, 12, 13, 15]
+    assert adjudicate(s, 4, 9, top9, cand, chunks=False) == "exact"
+    # positions 2 and 3 tie at 2.0: the other one is a near-tie
+    assert adjudicate(s, 4, 9, [1, 3, 4, 7, 8, 9, 12, 13, 15], cand, chunks=False) == "near_tie"
+    # dropping 12 (4.0) for 14 (1.5) is not a top-R set
+    assert adjudicate(s, 4, 9, [1, 2, 4, 7, 8, 9, 13, 14, 15], cand, chunks=False).startswith("fail")
+    # the Token2Chunk result is not what the ablation keeps
+    t2c = ko.token2chunk(s, np.array(cand), 9)
+    assert adjudicate(s, 4, 9, t2c, cand, chunks=False).startswith("fail")
