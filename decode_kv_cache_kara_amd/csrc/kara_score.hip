@@ -60,7 +60,11 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kRowsPerWave = 32;                 // one 32-row query tile per wave
+// 32-row query tiles per wave.  Two tiles halve the LDS fragment reads but
+// need 256 VGPRs (two waves per SIMD); on gfx950 one tile at four waves per
+// SIMD is as fast, so one it is.
+constexpr int kRT = 1;
+constexpr int kRowsPerWave = 32 * kRT;
 constexpr int kWaves = kScoreRowsPerChunk / kRowsPerWave;
 constexpr int kThreads = kWaves * 64;
 constexpr int kKeyTile = 64;
@@ -103,7 +107,7 @@ __device__ __forceinline__ int acc_row(int r, int lane) {
   return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 }
 
-// 16 waves of at most 128 VGPRs: four waves share each SIMD.
+// At most 128 VGPRs per wave: four waves share each SIMD.
 constexpr int kMinWavesPerEU = 4;
 
 template <typename T, int D, bool kUni>
@@ -157,7 +161,6 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerEU) void score_kernel(ScoreAr
 
   // Query fragments of this wave's rows, kept in registers for both passes.
   // Row r is window position r / G, head r % G of the group.
-  constexpr int kRT = 1;
   Frag qf[kRT][NK];
 #pragma unroll
   for (int qt = 0; qt < kRT; ++qt) {
@@ -211,35 +214,40 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerEU) void score_kernel(ScoreAr
     return *(const Frag*)p;
   };
 
-  // ---- software-pipelined schedule (one 32-row query tile per wave) -------
+  // ---- software-pipelined schedule -----------------------------------------
   // Within each wave the MFMAs of the next 32-key subtile are issued between
   // the exponentials of the current one (scheduling groups below), so the
-  // matrix core and the VALU of every SIMD work at the same time.  LDS holds
-  // three key tiles: the two being multiplied and the one being filled.
-  f32x16 accA, accB;
-  auto mma_sub = [&](f32x16& acc, int buf, int kt, auto keys_on_m) {
-    f32x16 z = {};
-    acc = z;
+  // matrix core and the VALU of every SIMD work at the same time.  Each key
+  // fragment read from LDS feeds the MFMAs of all kRT row tiles of the wave.
+  // LDS holds three key tiles: the two being multiplied and the one being
+  // filled.
+  typedef f32x16 Acc[kRT];
+  Acc accA, accB;
+  auto mma_sub = [&](Acc& acc, int buf, int kt, auto keys_on_m) {
+#pragma unroll
+    for (int qt = 0; qt < kRT; ++qt) {
+      f32x16 z = {};
+      acc[qt] = z;
+    }
 #pragma unroll
     for (int ks = 0; ks < NK; ++ks) {
       const Frag kf = kfrag(buf, kt, ks);
-      if constexpr (decltype(keys_on_m)::value) acc = M::run(kf, qf[0][ks], acc);
-      else acc = M::run(qf[0][ks], kf, acc);
+#pragma unroll
+      for (int qt = 0; qt < kRT; ++qt) {
+        if constexpr (decltype(keys_on_m)::value) acc[qt] = M::run(kf, qf[qt][ks], acc[qt]);
+        else acc[qt] = M::run(qf[qt][ks], kf, acc[qt]);
+      }
     }
   };
   auto interleave = [&]() {
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
     for (int i = 0; i < NK; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, kRT, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, 6 * kRT, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
   };
-  // Keeps a step's VALU results ahead of the point that follows (the compiler
-  // would otherwise sink the exponentials past the next barrier, away from the
-  // MFMAs they are meant to overlap).
-  auto pin = [](float x, float y) { asm volatile("" ::"v"(x), "v"(y)); };
   auto prologue = [&](int n_tiles) {
     load_tile(stage0, 0);
     store_tile(stage0, 0);
@@ -250,38 +258,57 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerEU) void score_kernel(ScoreAr
   };
 
   // ---------------- pass 1: row max and exp-sum over all W keys -------------
-  float m_run = -INFINITY, l_run = 0.0f;
-  // Unidirectional: this lane's query position, and the first position of
+  float m_run[kRT], l_run[kRT];
+  // Unidirectional: each lane's query positions, and the first position of
   // the wave (subtiles whose last key is past it cross the diagonal).
-  const int i_lane = (row0 + (lane & 31)) / G;
+  int i_lane[kRT];
+#pragma unroll
+  for (int qt = 0; qt < kRT; ++qt) {
+    m_run[qt] = -INFINITY;
+    l_run[qt] = 0.0f;
+    i_lane[qt] = (row0 + qt * 32 + (lane & 31)) / G;
+  }
   const int i_wave = row0 / G;
-  auto stats_sub = [&](f32x16& acc, int key0, auto masked) {
-    if constexpr (kUni) {
-      if (key0 + 31 > i_wave) {
-        // key = key0 + acc_row(r, lane) is seen iff key <= i_lane
-        const int lim = i_lane - key0 - 4 * (lane >> 5);
+  // Keeps a step's VALU results ahead of the point that follows (the compiler
+  // would otherwise sink the exponentials past the next barrier, away from the
+  // MFMAs they are meant to overlap).
+  auto pin = [&]() {
+#pragma unroll
+    for (int qt = 0; qt < kRT; ++qt) asm volatile("" ::"v"(m_run[qt]), "v"(l_run[qt]));
+  };
+  auto stats_sub = [&](Acc& accs, int key0, auto masked) {
+#pragma unroll
+    for (int qt = 0; qt < kRT; ++qt) {
+      f32x16& acc = accs[qt];
+      if constexpr (kUni) {
+        if (key0 + 31 > i_wave) {
+          // key = key0 + acc_row(r, lane) is seen iff key <= i_lane
+          const int lim = i_lane[qt] - key0 - 4 * (lane >> 5);
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (8 * (r >> 2) + (r & 3) > lim) acc[r] = -INFINITY;
+        }
+      } else if constexpr (decltype(masked)::value) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (8 * (r >> 2) + (r & 3) > lim) acc[r] = -INFINITY;
+          if (key0 + acc_row(r, lane) >= W) acc[r] = -INFINITY;
       }
-    } else if constexpr (decltype(masked)::value) {
+      float m0 = fmaxf(acc[0], acc[1]), m1 = fmaxf(acc[8], acc[9]);
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (key0 + acc_row(r, lane) >= W) acc[r] = -INFINITY;
+      for (int r = 2; r < 8; ++r) {
+        m0 = fmaxf(m0, acc[r]);
+        m1 = fmaxf(m1, acc[8 + r]);
+      }
+      const float mx = fmaxf(fmaxf(m0, m1), m_run[qt]);
+      // Only a masked subtile can leave a lane with no key seen so far.
+      float mc = mx * c;
+      if (kUni || decltype(masked)::value) mc = (mx == -INFINITY) ? 0.0f : mc;
+      float sp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sp[r & 3] += fast_exp2(fmaf(acc[r], c, -mc));
+      l_run[qt] = l_run[qt] * fast_exp2(m_run[qt] * c - mc) + ((sp[0] + sp[1]) + (sp[2] + sp[3]));
+      m_run[qt] = mx;
     }
-    float m0 = fmaxf(acc[0], acc[1]), m1 = fmaxf(acc[8], acc[9]);
-#pragma unroll
-    for (int r = 2; r < 8; ++r) {
-      m0 = fmaxf(m0, acc[r]);
-      m1 = fmaxf(m1, acc[8 + r]);
-    }
-    const float mx = fmaxf(fmaxf(m0, m1), m_run);
-    const float mc = (mx == -INFINITY) ? 0.0f : mx * c;
-    float sp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sp[r & 3] += fast_exp2(fmaf(acc[r], c, -mc));
-    l_run = l_run * fast_exp2(m_run * c - mc) + ((sp[0] + sp[1]) + (sp[2] + sp[3]));
-    m_run = mx;
   };
   // Key tiles: all of the window, or (unidirectional) up to the tile holding
   // the position of the workgroup's last row.  Uniform over the workgroup.
@@ -300,11 +327,11 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerEU) void score_kernel(ScoreAr
     mma_sub(accB, b0, 1, std::true_type());
     stats_sub(accA, t * kKeyTile, std::false_type());
     interleave();
-    pin(m_run, l_run);
+    pin();
     mma_sub(accA, b1, 0, std::true_type());
     stats_sub(accB, t * kKeyTile + 32, std::false_type());
     interleave();
-    pin(m_run, l_run);
+    pin();
     store_tile(stage0, b2);
     __syncthreads();
     load_tile(stage0, (t + 3 < T1 ? t + 3 : T1 - 1) * kKeyTile);
@@ -319,42 +346,52 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerEU) void score_kernel(ScoreAr
 
   // Merge the two lane halves (same query, disjoint keys) and publish the row
   // bias  m*c + log2(sum)  so that  p = exp2(x*c - bias).
-  {
-    const float mo = __shfl_xor(m_run, 32);
-    const float lo = __shfl_xor(l_run, 32);
-    const float mm = fmaxf(m_run, mo);
+#pragma unroll
+  for (int qt = 0; qt < kRT; ++qt) {
+    const float mo = __shfl_xor(m_run[qt], 32);
+    const float lo = __shfl_xor(l_run[qt], 32);
+    const float mm = fmaxf(m_run[qt], mo);
     const float mc = mm * c;
-    const float sum = l_run * fast_exp2(m_run * c - mc) + lo * fast_exp2(mo * c - mc);
-    const int row = row0 + (lane & 31);
+    const float sum = l_run[qt] * fast_exp2(m_run[qt] * c - mc) + lo * fast_exp2(mo * c - mc);
+    const int row = row0 + qt * 32 + (lane & 31);
     const float bias = (row < rows) ? mc + log2f(sum) : INFINITY;
-    if (lane < 32) bias_lds[wave * kRowsPerWave + lane] = bias;
+    if (lane < 32) bias_lds[wave * kRowsPerWave + qt * 32 + lane] = bias;
   }
   __syncthreads();
 
   // ---------------- pass 2: column sums over keys j < C ---------------------
-  float nbias[16];
+  float nbias[kRT][16];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) nbias[r] = -bias_lds[wave * kRowsPerWave + acc_row(r, lane)];
+  for (int qt = 0; qt < kRT; ++qt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      nbias[qt][r] = -bias_lds[wave * kRowsPerWave + qt * 32 + acc_row(r, lane)];
   float* out = a.out + ((size_t)unit * a.n_split + chunk) * C;
-  auto col_sub = [&](const f32x16& acc, int t, int kt) {
+  auto col_sub = [&](const Acc& accs, int t, int kt) {
     float sp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     bool plain = true;
     if constexpr (kUni) {
       const int key0 = t * kKeyTile + kt * 32;
       if (key0 + 31 > i_wave) {
-        // row = row0 + acc_row(r, lane) sees key = key0 + lane%32 iff key*G <= row
+        // row = row0 + qt*32 + acc_row(r, lane) sees key = key0 + lane%32
+        // iff key*G <= row
         plain = false;
-        const int lim = (key0 + (lane & 31)) * G - row0 - 4 * (lane >> 5);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = fast_exp2(fmaf(acc[r], c, nbias[r]));
-          sp[r & 3] += (8 * (r >> 2) + (r & 3) >= lim) ? e : 0.0f;
+        for (int qt = 0; qt < kRT; ++qt) {
+          const int lim = (key0 + (lane & 31)) * G - row0 - qt * 32 - 4 * (lane >> 5);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float e = fast_exp2(fmaf(accs[qt][r], c, nbias[qt][r]));
+            sp[r & 3] += (8 * (r >> 2) + (r & 3) >= lim) ? e : 0.0f;
+          }
         }
       }
     }
     if (plain) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sp[r & 3] += fast_exp2(fmaf(acc[r], c, nbias[r]));
+      for (int qt = 0; qt < kRT; ++qt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sp[r & 3] += fast_exp2(fmaf(accs[qt][r], c, nbias[qt][r]));
     }
     float col = (sp[0] + sp[1]) + (sp[2] + sp[3]);
     col += __shfl_xor(col, 32);

@@ -322,6 +322,51 @@ def apply_compaction(pool_arr, table, lens, new_table, window, protect, budget,
 
 
 # ----------------------------------------------------------------------------
+# Around the step: the window's query states, and decode attention over the
+# paged cache  [Summary, Methodology 1, Mechanism: the query states of all
+# window tokens score the region; Paper, Abstract: the compressed cache is
+# served through PagedAttention]
+# ----------------------------------------------------------------------------
+
+def window_queries(history, window):
+    """Query states of a sequence's last W tokens, in token order.
+
+    history: the query states [Lyr, Hq, D] of every token the sequence has
+    produced so far, oldest first.  Returns [Lyr, W, Hq, D].  (Under the
+    periodic schedule's watermark a window never reaches back into a region
+    that was compacted, so its tokens are the last W produced.)
+    """
+    if len(history) < window:
+        raise ValueError("fewer than W tokens produced")
+    return np.stack(history[-window:], axis=1)
+
+
+def decode_attention(q, pool_arr, table_row, length, layer, block_size):
+    """Attention of one decode step's queries over a sequence's cached tokens.
+
+    q: [Hq, D] query states of the sequence at `layer`.  The cache holds the
+    sequence's `length` tokens in logical order through `table_row`.  Query
+    head g reads KV head g // G: out[g] = sum_t softmax_t(q_g . k_t / sqrt(D))
+    v_t.  Returns float64 [Hq, D].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    Hq, D = q.shape
+    Hkv = pool_arr.shape[3]
+    G = Hq // Hkv
+    if length < 1:
+        raise ValueError("empty sequence")
+    out = np.zeros((Hq, D))
+    for h in range(Hkv):
+        k = logical_tokens(pool_arr, table_row, length, layer, 0, h, block_size).astype(np.float64)
+        v = logical_tokens(pool_arr, table_row, length, layer, 1, h, block_size).astype(np.float64)
+        for g in range(h * G, (h + 1) * G):
+            x = (k @ q[g]) / np.sqrt(D)
+            e = np.exp(x - x.max())
+            out[g] = (e / e.sum()) @ v
+    return out
+
+
+# ----------------------------------------------------------------------------
 # Periodic schedule  [Summary, Methodology 3, Periodic Compression Policy;
 # Summary, Methodology intro: compression only of recently generated context]
 # ----------------------------------------------------------------------------
