@@ -211,6 +211,9 @@ kara::ScoreArgs score_args(const kara_shape* sh, const kara_params* p, int32_t n
   a.n_units = n_seqs * sh->n_layers * sh->n_kv_heads;
   a.c = (float)(1.4426950408889634 / std::sqrt((double)sh->head_dim));
   a.unidirectional = (p->flags & KARA_UNIDIRECTIONAL) ? 1 : 0;
+  a.q_slots = nullptr;
+  a.q_counts = nullptr;
+  a.q_n_slots = 0;
   return a;
 }
 
@@ -316,14 +319,26 @@ size_t kara_workspace_bytes(const kara_shape* shape, const kara_params* params, 
   return layout(shape, params, n_seqs).total;
 }
 
-kara_status kara_compress(const kara_shape* shape, const kara_params* params, int32_t n_seqs,
-                          const void* q_window, void* kv_pool, int32_t n_blocks,
+}  // extern "C"
+
+namespace {
+
+// Where the window query states come from: one [S][Lyr][W][Hq][D] array, or
+// a ring of each sequence's last W query states.
+struct QuerySource {
+  const void* q;
+  const kara_query_ring* ring;  // null for the plain array
+};
+
+kara_status compress_impl(const kara_shape* shape, const kara_params* params, int32_t n_seqs,
+                          QuerySource qs, void* kv_pool, int32_t n_blocks,
                           const int32_t* block_table_h, const int32_t* block_table_d,
                           int32_t max_blocks, const int32_t* seq_lens_h, const int32_t* seq_lens_d,
                           kara_pool* pool, int32_t* new_block_table_h, int32_t* new_block_table_d,
                           int32_t* new_seq_lens_h, void* workspace, size_t workspace_bytes,
                           void* stream, float* scores_out_d, int32_t* cand_out_d,
                           int32_t* retained_out_d, void* const* stage_events) {
+  const void* q_window = qs.q;
   kara_status st;
   if ((st = check_shape(shape)) != KARA_OK) return st;
   if ((st = check_params(params)) != KARA_OK) return st;
@@ -332,10 +347,12 @@ kara_status kara_compress(const kara_shape* shape, const kara_params* params, in
   if ((st = check_sequences(shape, params, n_seqs, n_blocks, block_table_h, max_blocks, seq_lens_h, pool)) != KARA_OK)
     return st;
   if (n_seqs == 0) return KARA_OK;
+  if (qs.ring && (qs.ring->n_slots < 1 || !qs.ring->slots_d || !qs.ring->counts_d))
+    return fail(KARA_E_INVAL, "query ring: n_slots < 1 or slot/count arrays NULL");
   if (!q_window || !kv_pool || !block_table_d || !seq_lens_d || !new_block_table_d)
     return fail(KARA_E_INVAL, "device pointer NULL");
   if (!is_aligned(q_window, 16) || !is_aligned(kv_pool, 16))
-    return fail(KARA_E_INVAL, "q_window and kv_pool must be 16-byte aligned");
+    return fail(KARA_E_INVAL, "query states and kv_pool must be 16-byte aligned");
   const Workspace ws = layout(shape, params, n_seqs);
   if (!workspace || workspace_bytes < ws.total || !is_aligned(workspace, kAlign))
     return fail(KARA_E_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned", ws.total);
@@ -358,6 +375,11 @@ kara_status kara_compress(const kara_shape* shape, const kara_params* params, in
   if ((e = mark(0)) != hipSuccess) return hip_fail(e, "stage event");
   kara::ScoreArgs sa = score_args(shape, params, n_seqs, q_window, kv_pool, n_blocks, block_table_d,
                                   max_blocks, seq_lens_d, partials);
+  if (qs.ring) {
+    sa.q_slots = qs.ring->slots_d;
+    sa.q_counts = qs.ring->counts_d;
+    sa.q_n_slots = qs.ring->n_slots;
+  }
   if ((e = kara::launch_score(sa, shape->dtype, s)) != hipSuccess) return hip_fail(e, "score launch");
   if ((e = mark(1)) != hipSuccess) return hip_fail(e, "stage event");
   kara::SelectArgs se;
@@ -381,6 +403,148 @@ kara_status kara_compress(const kara_shape* shape, const kara_params* params, in
   if ((e = mark(3)) != hipSuccess) return hip_fail(e, "stage event");
   commit_plan(pool, plan);
   return KARA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kara_status kara_compress(const kara_shape* shape, const kara_params* params, int32_t n_seqs,
+                          const void* q_window, void* kv_pool, int32_t n_blocks,
+                          const int32_t* block_table_h, const int32_t* block_table_d,
+                          int32_t max_blocks, const int32_t* seq_lens_h, const int32_t* seq_lens_d,
+                          kara_pool* pool, int32_t* new_block_table_h, int32_t* new_block_table_d,
+                          int32_t* new_seq_lens_h, void* workspace, size_t workspace_bytes,
+                          void* stream, float* scores_out_d, int32_t* cand_out_d,
+                          int32_t* retained_out_d, void* const* stage_events) {
+  return compress_impl(shape, params, n_seqs, QuerySource{q_window, nullptr}, kv_pool, n_blocks,
+                       block_table_h, block_table_d, max_blocks, seq_lens_h, seq_lens_d, pool,
+                       new_block_table_h, new_block_table_d, new_seq_lens_h, workspace,
+                       workspace_bytes, stream, scores_out_d, cand_out_d, retained_out_d,
+                       stage_events);
+}
+
+kara_status kara_compress_ring(const kara_shape* shape, const kara_params* params, int32_t n_seqs,
+                               const kara_query_ring* ring, void* kv_pool, int32_t n_blocks,
+                               const int32_t* block_table_h, const int32_t* block_table_d,
+                               int32_t max_blocks, const int32_t* seq_lens_h,
+                               const int32_t* seq_lens_d, kara_pool* pool,
+                               int32_t* new_block_table_h, int32_t* new_block_table_d,
+                               int32_t* new_seq_lens_h, void* workspace, size_t workspace_bytes,
+                               void* stream, float* scores_out_d, int32_t* cand_out_d,
+                               int32_t* retained_out_d, void* const* stage_events) {
+  if (!ring) return fail(KARA_E_INVAL, "query ring is NULL");
+  return compress_impl(shape, params, n_seqs, QuerySource{ring->q_ring, ring}, kv_pool, n_blocks,
+                       block_table_h, block_table_d, max_blocks, seq_lens_h, seq_lens_d, pool,
+                       new_block_table_h, new_block_table_d, new_seq_lens_h, workspace,
+                       workspace_bytes, stream, scores_out_d, cand_out_d, retained_out_d,
+                       stage_events);
+}
+
+kara_status kara_append(const kara_shape* shape, int32_t window, int32_t n_seqs, int32_t layer,
+                        const void* q_d, const void* k_d, const void* v_d, void* kv_pool,
+                        int32_t n_blocks, const int32_t* block_table_d, int32_t max_blocks,
+                        const int32_t* positions_d, const kara_query_ring* ring, void* stream) {
+  kara_status st;
+  if ((st = check_shape(shape)) != KARA_OK) return st;
+  if (window < 1 || window > kara::kMaxWindow)
+    return fail(KARA_E_INVAL, "window %d outside [1, %d]", window, kara::kMaxWindow);
+  if (n_seqs < 0) return fail(KARA_E_INVAL, "n_seqs < 0");
+  if (layer < -1 || layer >= shape->n_layers)
+    return fail(KARA_E_INVAL, "layer %d outside [-1, %d)", layer, shape->n_layers);
+  if (n_blocks < 1 || max_blocks < 1) return fail(KARA_E_INVAL, "n_blocks and max_blocks must be >= 1");
+  if (!ring || ring->n_slots < 1) return fail(KARA_E_INVAL, "query ring NULL or without slots");
+  if (n_seqs == 0) return KARA_OK;
+  if (!q_d || !k_d || !v_d || !kv_pool || !block_table_d || !positions_d || !ring->q_ring ||
+      !ring->slots_d || !ring->counts_d)
+    return fail(KARA_E_INVAL, "device pointer NULL");
+  if (!is_aligned(q_d, 16) || !is_aligned(k_d, 16) || !is_aligned(v_d, 16) || !is_aligned(kv_pool, 16) ||
+      !is_aligned(ring->q_ring, 16))
+    return fail(KARA_E_INVAL, "state arrays, kv_pool and the ring must be 16-byte aligned");
+  kara::AppendArgs a;
+  a.q = q_d;
+  a.k = k_d;
+  a.v = v_d;
+  a.pool = kv_pool;
+  a.ring = ring->q_ring;
+  a.table = block_table_d;
+  a.positions = positions_d;
+  a.slots = ring->slots_d;
+  a.counts = ring->counts_d;
+  a.S = n_seqs;
+  a.Lyr = shape->n_layers;
+  a.n_lyr_in = layer >= 0 ? 1 : shape->n_layers;
+  a.layer = layer;
+  a.Hq = shape->n_q_heads;
+  a.Hkv = shape->n_kv_heads;
+  a.row_bytes = (int)(shape->head_dim * elt_size(shape));
+  a.bs = shape->block_size;
+  a.NB = n_blocks;
+  a.MB = max_blocks;
+  a.W = window;
+  a.n_slots = ring->n_slots;
+  const hipError_t e = kara::launch_append(a, (hipStream_t)stream);
+  return e == hipSuccess ? KARA_OK : hip_fail(e, "append launch");
+}
+
+size_t kara_attention_workspace_bytes(const kara_shape* shape, int32_t n_seqs, int32_t max_len) {
+  if (check_shape(shape) != KARA_OK || n_seqs < 0 || max_len < 1) return 0;
+  const size_t n_split = (size_t)ceil_div(max_len, kara::kAttnChunk);
+  const size_t parts = (size_t)n_seqs * shape->n_q_heads * n_split;
+  return align_up(parts * shape->head_dim * sizeof(float)) + align_up(parts * 2 * sizeof(float));
+}
+
+kara_status kara_decode_attention(const kara_shape* shape, int32_t n_seqs, int32_t layer,
+                                  const void* q_d, const void* kv_pool, int32_t n_blocks,
+                                  const int32_t* block_table_d, int32_t max_blocks,
+                                  const int32_t* seq_lens_h, const int32_t* seq_lens_d,
+                                  float* out_d, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  kara_status st;
+  if ((st = check_shape(shape)) != KARA_OK) return st;
+  if (shape->n_q_heads / shape->n_kv_heads > 8)
+    return fail(KARA_E_UNSUPPORTED, "decode attention supports at most 8 query heads per KV head");
+  if (n_seqs < 0) return fail(KARA_E_INVAL, "n_seqs < 0");
+  if (layer < 0 || layer >= shape->n_layers)
+    return fail(KARA_E_INVAL, "layer %d outside [0, %d)", layer, shape->n_layers);
+  if (n_blocks < 1 || max_blocks < 1) return fail(KARA_E_INVAL, "n_blocks and max_blocks must be >= 1");
+  if (n_seqs == 0) return KARA_OK;
+  if (!seq_lens_h) return fail(KARA_E_INVAL, "host lengths NULL");
+  int32_t max_len = 0;
+  for (int32_t b = 0; b < n_seqs; ++b) {
+    const int64_t L = seq_lens_h[b];
+    if (L < 1 || L > (int64_t)max_blocks * shape->block_size)
+      return fail(KARA_E_INVAL, "sequence %d: length %lld outside [1, max_blocks * block_size]", b, (long long)L);
+    max_len = L > max_len ? (int32_t)L : max_len;
+  }
+  if (!q_d || !kv_pool || !block_table_d || !seq_lens_d || !out_d)
+    return fail(KARA_E_INVAL, "device pointer NULL");
+  if (!is_aligned(q_d, 16) || !is_aligned(kv_pool, 16))
+    return fail(KARA_E_INVAL, "q and kv_pool must be 16-byte aligned");
+  const size_t need = kara_attention_workspace_bytes(shape, n_seqs, max_len);
+  if (!workspace || workspace_bytes < need || !is_aligned(workspace, kAlign))
+    return fail(KARA_E_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned", need);
+  kara::AttnArgs a;
+  a.q = q_d;
+  a.pool = kv_pool;
+  a.table = block_table_d;
+  a.lens = seq_lens_d;
+  a.S = n_seqs;
+  a.layer = layer;
+  a.Hq = shape->n_q_heads;
+  a.Hkv = shape->n_kv_heads;
+  a.D = shape->head_dim;
+  a.bs = shape->block_size;
+  a.NB = n_blocks;
+  a.MB = max_blocks;
+  a.n_split = ceil_div(max_len, kara::kAttnChunk);
+  a.c = (float)(1.4426950408889634 / std::sqrt((double)shape->head_dim));
+  const size_t parts = (size_t)n_seqs * a.Hq * a.n_split;
+  a.part_o = (float*)workspace;
+  a.part_ml = (float*)((char*)workspace + align_up(parts * a.D * sizeof(float)));
+  a.out = out_d;
+  const hipError_t e = kara::launch_attention(a, shape->dtype, (hipStream_t)stream);
+  return e == hipSuccess ? KARA_OK : hip_fail(e, "attention launch");
 }
 
 kara_status kara_score(const kara_shape* shape, const kara_params* params, int32_t n_seqs,

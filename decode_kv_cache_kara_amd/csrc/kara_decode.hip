@@ -1,0 +1,329 @@
+// The decode steps on either side of the compression step.
+//
+// append: one decode step's K and V rows go into the paged cache at the
+//   sequence's next physical position, and its query states into the
+//   sequence's ring of the last W query states ("Technical Summary: Kara",
+//   Methodology 1, Mechanism: all window tokens' query states score the
+//   region, so they are kept until the window is scored).  Pure 16-byte
+//   copies, one workgroup per (sequence, layer).
+//
+// decode attention: the attention of one decode step's query heads over a
+//   sequence's cached tokens, read through its block table (paper, Abstract:
+//   the compressed cache is served through PagedAttention).  It is bound by
+//   HBM: per token and KV head it reads one K and one V row (2 * D * elt
+//   bytes) and does 4 * G * D flops.  Layout of the work:
+//     * a workgroup takes 256 tokens of one (sequence, KV head) ("split");
+//       the G query heads of the group share every K/V row it reads;
+//     * 16 lanes hold one token's row as 16-byte pieces, so a wave loads 4
+//       tokens' rows per instruction, fully coalesced within a block row;
+//     * each lane group takes 4 tokens per step (8 loads in flight per lane),
+//       reduces the G dot products across its 16 lanes, and updates a running
+//       maximum, sum and output with one rescale per step;
+//     * lane groups, waves and then splits are merged with the usual
+//       (max, sum, output) rescaling; the split merge is a second kernel.
+//   Logits are kept in log2 units: the queries are pre-multiplied by
+//   log2(e) / sqrt(D) and exp2 is used throughout.
+
+#include "kara_internal.hpp"
+
+#include <cmath>
+
+namespace kara {
+namespace {
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// append
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
+  const int b = blockIdx.x / a.n_lyr_in;
+  const int li = blockIdx.x - b * a.n_lyr_in;
+  const int l = a.layer >= 0 ? a.layer : li;
+  const int tid = threadIdx.x;
+
+  int pos = a.positions[b];
+  const int max_pos = a.MB * a.bs - 1;
+  pos = pos < 0 ? 0 : (pos > max_pos ? max_pos : pos);
+  int blk = a.table[(size_t)b * a.MB + pos / a.bs];
+  blk = blk < 0 ? 0 : (blk >= a.NB ? a.NB - 1 : blk);
+  int slot = a.slots[b];
+  slot = slot < 0 ? 0 : (slot >= a.n_slots ? a.n_slots - 1 : slot);
+  int n = a.counts[b];
+  n = n < 0 ? 0 : n;
+  const int ring_pos = n % a.W;
+
+  const int row_pieces = a.row_bytes / 16;            // one head's row
+  const int q_pieces = a.Hq * row_pieces;
+  const int kv_pieces = a.Hkv * row_pieces;
+  const char* qs = (const char*)a.q + ((size_t)b * a.n_lyr_in + li) * q_pieces * 16;
+  char* qd = (char*)a.ring + (((size_t)slot * a.Lyr + l) * a.W + ring_pos) * q_pieces * 16;
+  for (int p = tid; p < q_pieces; p += 256)
+    *(u32x4*)(qd + (size_t)p * 16) = *(const u32x4*)(qs + (size_t)p * 16);
+
+  const size_t src_off = ((size_t)b * a.n_lyr_in + li) * kv_pieces * 16;
+  for (int p = tid; p < kv_pieces; p += 256) {
+    const int h = p / row_pieces, pc = p - h * row_pieces;
+#pragma unroll
+    for (int kv = 0; kv < 2; ++kv) {
+      const char* src = (const char*)(kv ? a.v : a.k) + src_off + (size_t)p * 16;
+      char* dst = (char*)a.pool +
+                  (((((size_t)l * 2 + kv) * a.NB + blk) * a.Hkv + h) * a.bs + pos % a.bs) * a.row_bytes +
+                  pc * 16;
+      *(u32x4*)dst = *(const u32x4*)src;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// decode attention
+// ---------------------------------------------------------------------------
+
+constexpr int kAttnThreads = 256;
+constexpr int kAttnWaves = kAttnThreads / 64;
+constexpr int kU = 4;  // tokens per lane group per step
+
+template <typename T>
+__device__ __forceinline__ void unpack(const u32x4& w, float* f);
+
+template <>
+__device__ __forceinline__ void unpack<__bf16>(const u32x4& w, float* f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+template <>
+__device__ __forceinline__ void unpack<float>(const u32x4& w, float* f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(w[i]);
+}
+
+// Merges (m2, l2, o2) into (m, l, o); maxima in log2 units, -inf = empty.
+template <int E>
+__device__ __forceinline__ void merge(float& m, float& l, float* o, float m2, float l2, const float* o2) {
+  const float mn = fmaxf(m, m2);
+  const float s1 = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - mn);
+  const float s2 = (m2 == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m2 - mn);
+  l = l * s1 + l2 * s2;
+#pragma unroll
+  for (int e = 0; e < E; ++e) o[e] = o[e] * s1 + o2[e] * s2;
+  m = mn;
+}
+
+template <typename T, int D, int G>
+__global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
+  constexpr int E = 16 / (int)sizeof(T);        // elements per 16-byte piece
+  constexpr int kLanes = D / E;                 // lanes per token row
+  constexpr int kGroups = 64 / kLanes;          // tokens per wave per load
+  constexpr int kRowBytes = D * (int)sizeof(T);
+  __shared__ float sh_m[kAttnWaves][G], sh_l[kAttnWaves][G];
+  __shared__ float sh_o[kAttnWaves][G][D];
+
+  const int split = blockIdx.x % a.n_split;
+  const int h = (blockIdx.x / a.n_split) % a.Hkv;
+  const int b = blockIdx.x / (a.n_split * a.Hkv);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int sub = lane % kLanes, grp = lane / kLanes;
+
+  int L = a.lens[b];
+  const int max_tok = a.MB * a.bs;
+  L = L < 1 ? 1 : (L > max_tok ? max_tok : L);
+  const int t0 = split * kAttnChunk;
+  const int t1 = min(L, t0 + kAttnChunk);
+
+  // this lane's piece of the G query rows, in log2 units
+  float q[G][E];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const u32x4 w = *(const u32x4*)((const char*)a.q +
+                                    (((size_t)b * a.Hq + h * G + g) * D + sub * E) * sizeof(T));
+    unpack<T>(w, q[g]);
+#pragma unroll
+    for (int e = 0; e < E; ++e) q[g][e] *= a.c;
+  }
+  float m[G], l[G], o[G][E];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m[g] = -INFINITY;
+    l[g] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[g][e] = 0.0f;
+  }
+
+  const int32_t* trow = a.table + (size_t)b * a.MB;
+  const char* kbase = (const char*)a.pool + ((size_t)a.layer * 2 * a.NB * a.Hkv + h) * a.bs * kRowBytes;
+  const size_t v_off = (size_t)a.NB * a.Hkv * a.bs * kRowBytes;
+  const size_t blk_bytes = (size_t)a.Hkv * a.bs * kRowBytes;
+  constexpr int kStep = kAttnWaves * kGroups * kU;   // tokens per workgroup step
+
+  for (int base = t0 + (wave * kGroups + grp) * kU; base - (wave * kGroups + grp) * kU < t1; base += kStep) {
+    u32x4 kw[kU], vw[kU];
+    bool ok[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int t = base + u;
+      ok[u] = t < t1;
+      const int tc = ok[u] ? t : t1 - 1;
+      int blk = trow[tc / a.bs];
+      blk = blk < 0 ? 0 : (blk >= a.NB ? a.NB - 1 : blk);
+      const char* p = kbase + (size_t)blk * blk_bytes + (size_t)(tc % a.bs) * kRowBytes + sub * 16;
+      kw[u] = __builtin_nontemporal_load((const u32x4*)p);
+      vw[u] = __builtin_nontemporal_load((const u32x4*)(p + v_off));
+    }
+    float x[kU][G];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      float kf[E];
+      unpack<T>(kw[u], kf);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float d = 0.0f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) d = fmaf(q[g][e], kf[e], d);
+        x[u][g] = d;
+      }
+    }
+#pragma unroll
+    for (int off = kLanes / 2; off >= 1; off >>= 1)
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+#pragma unroll
+        for (int g = 0; g < G; ++g) x[u][g] += __shfl_xor(x[u][g], off);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float mx = m[g];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        if (!ok[u]) x[u][g] = -INFINITY;
+        mx = fmaxf(mx, x[u][g]);
+      }
+      if (mx == -INFINITY) continue;              // nothing seen yet in this lane group
+      const float sc = __builtin_amdgcn_exp2f(m[g] - mx);
+      l[g] *= sc;
+#pragma unroll
+      for (int e = 0; e < E; ++e) o[g][e] *= sc;
+      m[g] = mx;
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      float vf[E];
+      unpack<T>(vw[u], vf);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float p = (x[u][g] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(x[u][g] - m[g]);
+        l[g] += p;
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[g][e] = fmaf(p, vf[e], o[g][e]);
+      }
+    }
+  }
+
+  // merge the lane groups of the wave (same pieces, different tokens)
+#pragma unroll
+  for (int off = kLanes; off < 64; off <<= 1) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float m2 = __shfl_xor(m[g], off), l2 = __shfl_xor(l[g], off);
+      float o2[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) o2[e] = __shfl_xor(o[g][e], off);
+      merge<E>(m[g], l[g], o[g], m2, l2, o2);
+    }
+  }
+  if (grp == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      if (sub == 0) {
+        sh_m[wave][g] = m[g];
+        sh_l[wave][g] = l[g];
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) sh_o[wave][g][sub * E + e] = o[g][e];
+    }
+  }
+  __syncthreads();
+  // merge the waves and write this split's (max, sum, output) per query head
+  const size_t part = (size_t)(b * a.Hq + h * G) * a.n_split + split;
+  for (int i = tid; i < G * D; i += kAttnThreads) {
+    const int g = i / D, d = i - g * D;
+    float mm = sh_m[0][g], ll = sh_l[0][g], oo = sh_o[0][g][d];
+#pragma unroll
+    for (int w = 1; w < kAttnWaves; ++w) merge<1>(mm, ll, &oo, sh_m[w][g], sh_l[w][g], &sh_o[w][g][d]);
+    const size_t pg = part + (size_t)g * a.n_split;
+    a.part_o[pg * D + d] = oo;
+    if (d == 0) {
+      a.part_ml[2 * pg] = mm;
+      a.part_ml[2 * pg + 1] = ll;
+    }
+  }
+}
+
+// out[b][g] = merge over splits; one workgroup per (sequence, query head).
+template <int D>
+__global__ __launch_bounds__(D) void combine_kernel(AttnArgs a) {
+  const int bg = blockIdx.x;
+  const int d = threadIdx.x;
+  const size_t p0 = (size_t)bg * a.n_split;
+  float mm = -INFINITY;
+  for (int s = 0; s < a.n_split; ++s) mm = fmaxf(mm, a.part_ml[2 * (p0 + s)]);
+  float num = 0.0f, den = 0.0f;
+  for (int s = 0; s < a.n_split; ++s) {
+    const float ms = a.part_ml[2 * (p0 + s)];
+    if (ms == -INFINITY) continue;
+    const float w = __builtin_amdgcn_exp2f(ms - mm);
+    den = fmaf(a.part_ml[2 * (p0 + s) + 1], w, den);
+    num = fmaf(a.part_o[(p0 + s) * D + d], w, num);
+  }
+  a.out[(size_t)bg * D + d] = num / den;
+}
+
+template <typename T, int D, int G>
+hipError_t launch_attention_g(const AttnArgs& a, hipStream_t s) {
+  const unsigned grid = (unsigned)a.S * a.Hkv * a.n_split;
+  hipLaunchKernelGGL((attention_kernel<T, D, G>), dim3(grid), dim3(kAttnThreads), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((combine_kernel<D>), dim3((unsigned)a.S * a.Hq), dim3(D), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_attention_d(const AttnArgs& a, hipStream_t s) {
+  switch (a.Hq / a.Hkv) {
+    case 1: return launch_attention_g<T, D, 1>(a, s);
+    case 2: return launch_attention_g<T, D, 2>(a, s);
+    case 3: return launch_attention_g<T, D, 3>(a, s);
+    case 4: return launch_attention_g<T, D, 4>(a, s);
+    case 5: return launch_attention_g<T, D, 5>(a, s);
+    case 6: return launch_attention_g<T, D, 6>(a, s);
+    case 7: return launch_attention_g<T, D, 7>(a, s);
+    case 8: return launch_attention_g<T, D, 8>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t stream) {
+  if (a.S == 0) return hipSuccess;
+  hipLaunchKernelGGL(append_kernel, dim3((unsigned)a.S * a.n_lyr_in), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attention(const AttnArgs& a, int dtype, hipStream_t stream) {
+  if (a.S == 0) return hipSuccess;
+  if (dtype == 1) {
+    if (a.D == 128) return launch_attention_d<__bf16, 128>(a, stream);
+    if (a.D == 64) return launch_attention_d<__bf16, 64>(a, stream);
+  } else {
+    if (a.D == 128) return launch_attention_d<float, 128>(a, stream);
+    if (a.D == 64) return launch_attention_d<float, 64>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kara

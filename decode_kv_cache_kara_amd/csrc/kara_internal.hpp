@@ -25,6 +25,11 @@ struct ScoreArgs {
   int n_units;            // S * Lyr * Hkv
   float c;                // log2(e) / sqrt(D)
   int unidirectional;     // 1: query i sees window keys j <= i only
+  // Query states from a ring instead of q: sequence b's window row i is ring
+  // position (q_counts[b] - W + i) mod W of ring row q_slots[b].
+  const int32_t* q_slots; // null: q is [S][Lyr][W][Hq][D]
+  const int32_t* q_counts;
+  int q_n_slots;
 };
 
 inline int score_chunks(int G, int W) {
@@ -52,6 +57,38 @@ struct SelectArgs {
 };
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
+
+struct AppendArgs {
+  const void* q;              // [S][n_lyr_in][Hq][D]
+  const void* k;              // [S][n_lyr_in][Hkv][D]
+  const void* v;
+  void* pool;                 // [Lyr][2][NB][Hkv][bs][D]
+  void* ring;                 // [n_slots][Lyr][W][Hq][D]
+  const int32_t* table;       // [S][MB]
+  const int32_t* positions;   // [S] physical position of the new token
+  const int32_t* slots;       // [S]
+  const int32_t* counts;      // [S] index of the new token among those produced
+  int S, Lyr, n_lyr_in, layer, Hq, Hkv, row_bytes, bs, NB, MB, W, n_slots;
+};
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
+
+// Tokens of one (sequence, KV head) per decode-attention workgroup.
+constexpr int kAttnChunk = 256;
+
+struct AttnArgs {
+  const void* q;              // [S][Hq][D]
+  const void* pool;           // [Lyr][2][NB][Hkv][bs][D]
+  const int32_t* table;       // [S][MB]
+  const int32_t* lens;        // [S]
+  float* part_o;              // [S][Hq][n_split][D]
+  float* part_ml;             // [S][Hq][n_split][2]: max (log2 units), sum
+  float* out;                 // [S][Hq][D]
+  int S, layer, Hq, Hkv, D, bs, NB, MB, n_split;
+  float c;                    // log2(e) / sqrt(D)
+};
+
+hipError_t launch_attention(const AttnArgs& a, int dtype, hipStream_t stream);
 
 struct CompactArgs {
   void* pool;                 // [Lyr][2][NB][Hkv][bs][D]

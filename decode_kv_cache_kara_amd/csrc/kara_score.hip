@@ -42,6 +42,10 @@
 // cross a wave's diagonal are masked element by element, and the partial
 // column sums of keys past the last tile are written as zeros.
 //
+// The window's query states come either as one array per call or from a ring
+// that keeps each sequence's last W query states (row i of the window is then
+// ring position (count - W + i) mod W); only the row addresses differ.
+//
 // One workgroup scores 512 rows of one unit.  The workgroups of a unit are
 // dispatched back to back onto the same XCD (block ids are interleaved across
 // the 8 XCDs) so that unit's K rows are fetched from HBM once and then served
@@ -149,7 +153,18 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerEU) void score_kernel(ScoreAr
   L = L < W ? W : (L > max_tok ? max_tok : L);
   const int start = L - W;
   const int32_t* trow = a.table + (size_t)b * a.MB;
-  const T* qbase = (const T*)a.q + (size_t)bl * W * a.Hq * D + (size_t)h * G * D;
+  // Window query rows: row i of the window is q[b][l][i], or, from a ring,
+  // ring position (count - W + i) mod W of the sequence's ring row.
+  size_t q_row0 = (size_t)bl * W;
+  int ring_off = 0;
+  if (a.q_slots) {
+    int slot = a.q_slots[b];
+    slot = slot < 0 ? 0 : (slot >= a.q_n_slots ? a.q_n_slots - 1 : slot);
+    const int n = a.q_counts[b];
+    q_row0 = ((size_t)slot * a.Lyr + l) * W;
+    ring_off = (n < 0 ? 0 : n) % W;               // (n - W + i) mod W = (n + i) mod W
+  }
+  const T* qbase = (const T*)a.q + q_row0 * a.Hq * D + (size_t)h * G * D;
   const char* kbase = (const char*)a.pool +
       ((size_t)l * 2 * a.NB * a.Hkv * a.bs + (size_t)h * a.bs) * D * sizeof(T);
   const size_t blk_bytes = (size_t)a.Hkv * a.bs * D * sizeof(T);
@@ -167,7 +182,8 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerEU) void score_kernel(ScoreAr
     const int row = row0 + qt * 32 + (lane & 31);
     if (row < rows) {
       const int i = row / G, g = row - (row / G) * G;
-      const T* p = qbase + ((size_t)i * a.Hq + g) * D + (lane >> 5) * M::kPerLane;
+      const int slot_i = i + ring_off < W ? i + ring_off : i + ring_off - W;
+      const T* p = qbase + ((size_t)slot_i * a.Hq + g) * D + (lane >> 5) * M::kPerLane;
 #pragma unroll
       for (int ks = 0; ks < NK; ++ks) qf[qt][ks] = *(const Frag*)(p + ks * M::kStep);
     } else {

@@ -49,6 +49,11 @@ class kara_params(ctypes.Structure):
                 ("flags", ctypes.c_int32)]
 
 
+class kara_query_ring(ctypes.Structure):
+    _fields_ = [("q_ring", ctypes.c_void_p), ("n_slots", ctypes.c_int32),
+                ("slots_d", ctypes.c_void_p), ("counts_d", ctypes.c_void_p)]
+
+
 # kara_params.flags: the two ablations (0 = the method itself)
 UNIDIRECTIONAL = 1
 NO_CHUNKS = 2
@@ -73,6 +78,11 @@ _SIGS = {
     "kara_token2chunk": (_I, [_I, _I, _I, _I, _P, _P, _P, _P]),
     "kara_paged_compact": (_I, [_P, _P, _I, _P, _I, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
     "kara_schedule_step": (_I, [ctypes.c_int64, _I, _I, _I, _P, _P, _P, _P, _P]),
+    "kara_append": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _I, _P, _I, _P, _P, _P]),
+    "kara_compress_ring": (_I, [_P, _P, _I, _P, _P, _I, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P,
+                                ctypes.c_size_t, _P, _P, _P, _P, _P]),
+    "kara_attention_workspace_bytes": (ctypes.c_size_t, [_P, _I, _I]),
+    "kara_decode_attention": (_I, [_P, _I, _I, _P, _P, _I, _P, _I, _P, _P, _P, _P, ctypes.c_size_t, _P]),
 }
 EXPORTED = tuple(_SIGS)
 
@@ -268,3 +278,58 @@ def kara_schedule_step(step, period, window, seq_lens, watermarks, selected):
                                    _host_i32(seq_lens, "seq_lens"), _host_i32(watermarks, "watermarks"),
                                    sel.data_ptr(), out.data_ptr(), ctypes.byref(nb)))
     return out[:nb.value].tolist()
+
+
+class QueryRing:
+    """Device ring of every sequence slot's last W query states (see
+    kara_query_ring in include/kara.h): q [n_slots][Lyr][W][Hq][D]."""
+
+    def __init__(self, q, slots_d, counts_d):
+        self.q, self.slots_d, self.counts_d = q, slots_d, counts_d
+        self.struct = kara_query_ring(_dev(q, "q_ring"), q.shape[0], _dev(slots_d, "slots_d", torch.int32),
+                                      _dev(counts_d, "counts_d", torch.int32))
+
+
+def kara_append(shape, window, layer, q, k, v, kv_pool, block_table_d, positions_d, ring, stream=None):
+    """One decode step's states: layer >= 0 with q [S][Hq][D], k/v [S][Hkv][D],
+    or layer = -1 with a layer axis after S."""
+    n_seqs = positions_d.numel()
+    _check(_lib.kara_append(ctypes.byref(shape), int(window), n_seqs, int(layer), _dev(q, "q"),
+                            _dev(k, "k"), _dev(v, "v"), _dev(kv_pool, "kv_pool"), kv_pool.shape[2],
+                            _dev(block_table_d, "block_table_d", torch.int32), block_table_d.shape[1],
+                            _dev(positions_d, "positions_d", torch.int32), ctypes.byref(ring.struct),
+                            _stream(stream)))
+
+
+def kara_compress_ring(shape, params, ring, kv_pool, block_table_h, block_table_d, seq_lens_h,
+                       seq_lens_d, pool, new_block_table_h, new_block_table_d, new_seq_lens_h,
+                       workspace, stream=None, scores_out=None, cand_out=None, retained_out=None,
+                       stage_events=None):
+    n_seqs = seq_lens_h.numel()
+    ev = (_P * 4)(*stage_events) if stage_events is not None else None
+    _check(_lib.kara_compress_ring(
+        ctypes.byref(shape), ctypes.byref(params), n_seqs, ctypes.byref(ring.struct),
+        _dev(kv_pool, "kv_pool"), kv_pool.shape[2], _host_i32(block_table_h, "block_table_h"),
+        _dev(block_table_d, "block_table_d", torch.int32), block_table_h.shape[1],
+        _host_i32(seq_lens_h, "seq_lens_h"), _dev(seq_lens_d, "seq_lens_d", torch.int32),
+        pool.handle, _host_i32(new_block_table_h, "new_block_table_h"),
+        _dev(new_block_table_d, "new_block_table_d", torch.int32),
+        _host_i32(new_seq_lens_h, "new_seq_lens_h"), _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size() if workspace is not None else 0,
+        _stream(stream), _dev(scores_out, "scores_out", torch.float32),
+        _dev(cand_out, "cand_out", torch.int32), _dev(retained_out, "retained_out", torch.int32), ev))
+
+
+def kara_attention_workspace_bytes(shape, n_seqs, max_len):
+    return int(_lib.kara_attention_workspace_bytes(ctypes.byref(shape), int(n_seqs), int(max_len)))
+
+
+def kara_decode_attention(shape, layer, q, kv_pool, block_table_d, seq_lens_h, seq_lens_d, out,
+                          workspace, stream=None):
+    n_seqs = seq_lens_h.numel()
+    _check(_lib.kara_decode_attention(
+        ctypes.byref(shape), n_seqs, int(layer), _dev(q, "q"), _dev(kv_pool, "kv_pool"), kv_pool.shape[2],
+        _dev(block_table_d, "block_table_d", torch.int32), block_table_d.shape[1],
+        _host_i32(seq_lens_h, "seq_lens_h"), _dev(seq_lens_d, "seq_lens_d", torch.int32),
+        _dev(out, "out", torch.float32), _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size() if workspace is not None else 0, _stream(stream)))

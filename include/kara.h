@@ -242,6 +242,87 @@ kara_status kara_paged_compact(const kara_shape* shape, const kara_params* param
                                int32_t* new_block_table_h, int32_t* new_block_table_d,
                                int32_t* new_seq_lens_h, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Around the step: keeping the window's query states, and decode attention
+ * over the (compressed) paged cache.
+ * ------------------------------------------------------------------------ */
+
+/* Window query states kept on the device ("Technical Summary: Kara",
+ * Methodology 1, Mechanism: the query states of all window tokens score the
+ * region, so they must still exist when the window is scored).  Each sequence
+ * slot holds the query states of its last W produced tokens: token n (counted
+ * over everything the sequence has produced, whether or not it was later
+ * compacted away) sits at ring position n mod W.
+ *   q_ring    dev [n_slots][n_layers][W][n_q_heads][head_dim] (dtype)
+ *   slots_d   dev [n_seqs] ring row of each sequence of the call
+ *   counts_d  dev [n_seqs] tokens produced so far: for kara_compress_ring the
+ *             count N, so the window is tokens N - W .. N - 1; for
+ *             kara_append the index of the token being appended.
+ * Under the periodic schedule's watermark a window never reaches back into a
+ * compacted region, so its W tokens are the last W produced and the trailing
+ * W physical tokens of the cache.  Device indices are clamped (slots to
+ * [0, n_slots)), never dereferenced out of bounds. */
+typedef struct {
+  void* q_ring;
+  int32_t n_slots;
+  const int32_t* slots_d;
+  const int32_t* counts_d;
+} kara_query_ring;
+
+/* One decode step's states of n_seqs sequences, at one layer (layer in
+ * [0, n_layers): q_d [n_seqs][Hq][D], k_d and v_d [n_seqs][Hkv][D]) or at
+ * every layer (layer = -1: q_d [n_seqs][n_layers][Hq][D], k_d and v_d
+ * [n_seqs][n_layers][Hkv][D]), all dev and of the shape's dtype.  K and V go
+ * to physical position positions_d[b] (dev) of sequence b through
+ * block_table_d (dev [n_seqs][max_blocks]; the caller has allocated the
+ * block); the query states go to ring position counts_d[b] mod W of ring row
+ * slots_d[b].  Positions are clamped to the table and block ids to the pool.
+ * Errors: KARA_E_INVAL, KARA_E_UNSUPPORTED (nothing written), KARA_E_HIP. */
+kara_status kara_append(const kara_shape* shape, int32_t window, int32_t n_seqs, int32_t layer,
+                        const void* q_d, const void* k_d, const void* v_d, void* kv_pool,
+                        int32_t n_blocks, const int32_t* block_table_d, int32_t max_blocks,
+                        const int32_t* positions_d, const kara_query_ring* ring, void* stream);
+
+/* kara_compress with the window query states read from a ring (above)
+ * instead of a [n_seqs][n_layers][W][Hq][D] array: row i of sequence b's
+ * window is ring position (counts_d[b] - W + i) mod W of ring row
+ * slots_d[b].  Every other argument, output and error as for kara_compress. */
+kara_status kara_compress_ring(const kara_shape* shape, const kara_params* params, int32_t n_seqs,
+                               const kara_query_ring* ring, void* kv_pool, int32_t n_blocks,
+                               const int32_t* block_table_h, const int32_t* block_table_d,
+                               int32_t max_blocks, const int32_t* seq_lens_h,
+                               const int32_t* seq_lens_d, kara_pool* pool,
+                               int32_t* new_block_table_h, int32_t* new_block_table_d,
+                               int32_t* new_seq_lens_h, void* workspace, size_t workspace_bytes,
+                               void* stream, float* scores_out_d, int32_t* cand_out_d,
+                               int32_t* retained_out_d, void* const* stage_events);
+
+/* Device workspace bytes kara_decode_attention needs for n_seqs sequences of
+ * at most max_len tokens (0 on invalid arguments). */
+size_t kara_attention_workspace_bytes(const kara_shape* shape, int32_t n_seqs, int32_t max_len);
+
+/* Decode attention at one layer over every sequence's cached tokens, read
+ * through its block table (Paper, Abstract: the compressed cache is served
+ * through PagedAttention; this is how the compacted tables are consumed).
+ *   q_d          dev [n_seqs][Hq][D] query states (dtype)
+ *   out_d        dev [n_seqs][Hq][D] float32:
+ *                out[b][g] = sum_t softmax_t(q[b][g] . k_t / sqrt(D)) v_t
+ *                over tokens t < lens[b] of KV head g / G at `layer`
+ *   seq_lens_h   host [n_seqs] lengths in [1, max_blocks * bs] (sizes the
+ *                launch); seq_lens_d the device copy (read by the kernels,
+ *                clamped to the same range)
+ *   workspace    dev, kara_attention_workspace_bytes(shape, n_seqs,
+ *                max(seq_lens_h)) bytes, 256-byte aligned.
+ * Supported: n_q_heads / n_kv_heads <= 8.  Block ids are clamped to the pool.
+ * Errors: KARA_E_INVAL, KARA_E_UNSUPPORTED, KARA_E_WORKSPACE (nothing
+ * written), KARA_E_HIP. */
+kara_status kara_decode_attention(const kara_shape* shape, int32_t n_seqs, int32_t layer,
+                                  const void* q_d, const void* kv_pool, int32_t n_blocks,
+                                  const int32_t* block_table_d, int32_t max_blocks,
+                                  const int32_t* seq_lens_h, const int32_t* seq_lens_d,
+                                  float* out_d, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
 /* Periodic compression schedule ("Technical Summary: Kara", Methodology 3,
  * Periodic Compression Policy: every fixed number of decode steps the
  * trailing blocks of selected sequences are compressed; Summary, Methodology
