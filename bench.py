@@ -86,6 +86,44 @@ def cpu_baseline(cfg, n_layers_sample, seed, n_seqs_sample=3, flags=0):
                        f"shapes (L={[int(x) for x in lens]}), {dt:.1f} s, scaled to the full layer count")}
 
 
+def decode_attention_roofline(ses, wl, launches=36):
+    """Decode attention over the cache as the last compression step left it
+    (new tables and lengths): HBM bytes per launch = K and V rows of every
+    cached token of one layer, averaged over `launches` launches that cycle
+    through the layers; timed with HIP events on the launch stream."""
+    import torch
+
+    from decode_kv_cache_kara_amd import kara
+
+    S, Hq, D, Lyr = wl.n_seqs, wl.n_q_heads, wl.head_dim, wl.n_layers
+    lens_h = ses.new_lens_h.clone()
+    lens_d = lens_h.cuda()
+    table_d = ses.new_table_d
+    g = torch.Generator(device="cuda").manual_seed(99)
+    q = (torch.randn((S, Hq, D), generator=g, device="cuda") * 0.1).to(wl.dtype)
+    out = torch.empty((S, Hq, D), device="cuda")
+    ws = torch.empty(kara.kara_attention_workspace_bytes(ses.shape, S, int(lens_h.max())), dtype=torch.uint8,
+                     device="cuda")
+    stream = torch.cuda.current_stream()
+    for l in range(3):
+        kara.kara_decode_attention(ses.shape, l % Lyr, q, wl.pool, table_d, lens_h, lens_d, out, ws, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for k in range(launches):
+        kara.kara_decode_attention(ses.shape, k % Lyr, q, wl.pool, table_d, lens_h, lens_d, out, ws, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / launches
+    tokens = int(lens_h.sum())
+    nbytes = 2.0 * tokens * wl.n_kv_heads * D * wl.pool.element_size()
+    gbs = nbytes / (ms / 1e3) / 1e9
+    return {"bound": "hbm", "kernel": "attention_kernel+combine_kernel", "achieved": round(gbs, 1),
+            "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "ms_per_launch": round(ms, 4), "algorithmic_bytes_per_launch": nbytes,
+            "cached_tokens": tokens, "note": "one layer of all sequences over the compacted cache"}
+
+
 def run_trace(args, out_base):
     """Config 4: the periodic-compression serving trace.  A step is one
     compression event's kara_compress call; `--warmup` events run untimed,
@@ -292,6 +330,9 @@ def main():
                              "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(compact_gbs / PEAK_HBM_GBS, 4),
                              "algorithmic_bytes_per_launch": compact_bytes},
     }
+    out["decode_attention"] = decode_attention_roofline(ses, wl)
+    log(f"decode attention over the compacted cache: {out['decode_attention']['ms_per_launch']:.3f} ms/layer, "
+        f"{out['decode_attention']['achieved']:.0f} GB/s")
     if not args.no_cpu_baseline:
         del ses, wl
         torch.cuda.empty_cache()
