@@ -124,6 +124,34 @@ def decode_attention_roofline(ses, wl, launches=36):
             "cached_tokens": tokens, "note": "one layer of all sequences over the compacted cache"}
 
 
+def policy_sim(out, wl):
+    """Periodic vs threshold vs no compression on the native serving
+    simulator, with per-step costs from this run's measurements scaled to
+    Distill-Llama-8B (32 layers, 8 KV heads of 128, like the measured slice):
+    decode attention per cached token from `decode_attention`, one
+    sequence's compression from the step time; the fixed per-step part
+    (reading 16 GB of bf16 weights at 8 TB/s, 2 ms) is an assumption."""
+    from decode_kv_cache_kara_amd import policy
+
+    layers = 32
+    att = out["decode_attention"]
+    per_token = att["ms_per_launch"] / att["cached_tokens"] * layers
+    per_seq = out["ms_per_step"] / wl.n_seqs * layers / wl.n_layers
+    costs = dict(decode_ms_fixed=2.0, decode_ms_per_token=per_token, compress_ms_per_seq=per_seq,
+                 compress_ms_per_key=per_seq / wl.window)
+    rows = []
+    for pol, mb, sm in policy.compare(costs):
+        rows.append({"policy": pol, "max_batch": mb, "tokens_per_s": round(sm["tokens_per_s"], 1),
+                     "compressions": sm["compressions"], "compress_share": round(sm["compress_share"], 5),
+                     "preemptions": sm["preemptions"], "mean_running": round(sm["mean_active"], 1)})
+    best = {p: max((r for r in rows if r["policy"] == p), key=lambda r: r["tokens_per_s"]) for p in
+            ("periodic", "threshold", "none")}
+    log("policy sim (best tokens/s): " + ", ".join(f"{p} {b['tokens_per_s']:.0f} at batch {b['max_batch']}"
+                                                   for p, b in best.items()))
+    return {"costs_ms": {k: float(f"{v:.6g}") for k, v in costs.items()}, "workload": policy.WORKLOAD,
+            "rows": rows}
+
+
 def run_trace(args, out_base):
     """Config 4: the periodic-compression serving trace.  A step is one
     compression event's kara_compress call; `--warmup` events run untimed,
@@ -333,6 +361,8 @@ def main():
     out["decode_attention"] = decode_attention_roofline(ses, wl)
     log(f"decode attention over the compacted cache: {out['decode_attention']['ms_per_launch']:.3f} ms/layer, "
         f"{out['decode_attention']['achieved']:.0f} GB/s")
+    if args.flags == 0:
+        out["policy_sim"] = policy_sim(out, wl)
     if not args.no_cpu_baseline:
         del ses, wl
         torch.cuda.empty_cache()

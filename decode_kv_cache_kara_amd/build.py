@@ -9,7 +9,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkara.so")
-SOURCES = ["kara_api.cpp", "kara_score.hip", "kara_select.hip", "kara_compact.hip", "kara_decode.hip"]
+SOURCES = ["kara_api.cpp", "kara_score.hip", "kara_select.hip", "kara_compact.hip", "kara_decode.hip",
+           "kara_policy.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

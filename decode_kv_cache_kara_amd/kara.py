@@ -54,6 +54,30 @@ class kara_query_ring(ctypes.Structure):
                 ("slots_d", ctypes.c_void_p), ("counts_d", ctypes.c_void_p)]
 
 
+class kara_sim_config(ctypes.Structure):
+    _fields_ = [("policy", ctypes.c_int32), ("n_requests", ctypes.c_int32), ("max_batch", ctypes.c_int32),
+                ("cap_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32), ("prompt_len", ctypes.c_int32),
+                ("gen_min", ctypes.c_int32), ("gen_max", ctypes.c_int32), ("seed", ctypes.c_uint64),
+                ("window", ctypes.c_int32), ("protect", ctypes.c_int32), ("budget", ctypes.c_int32),
+                ("period", ctypes.c_int32), ("threshold", ctypes.c_int32), ("keep", ctypes.c_int32),
+                ("decode_ms_fixed", ctypes.c_double), ("decode_ms_per_token", ctypes.c_double),
+                ("compress_ms_per_seq", ctypes.c_double), ("compress_ms_per_key", ctypes.c_double),
+                ("max_steps", ctypes.c_int32)]
+
+
+class kara_sim_result(ctypes.Structure):
+    _fields_ = [("steps", ctypes.c_int64), ("tokens", ctypes.c_int64), ("compressions", ctypes.c_int64),
+                ("stalls", ctypes.c_int64), ("peak_blocks", ctypes.c_int64), ("preemptions", ctypes.c_int64),
+                ("wasted", ctypes.c_int64), ("finished", ctypes.c_int32),
+                ("total_ms", ctypes.c_double), ("compress_ms", ctypes.c_double), ("mean_active", ctypes.c_double)]
+
+
+KARA_POLICY_PERIODIC = 0
+KARA_POLICY_THRESHOLD = 1
+KARA_POLICY_NONE = 2
+_POLICIES = {"periodic": KARA_POLICY_PERIODIC, "threshold": KARA_POLICY_THRESHOLD, "none": KARA_POLICY_NONE}
+
+
 # kara_params.flags: the two ablations (0 = the method itself)
 UNIDIRECTIONAL = 1
 NO_CHUNKS = 2
@@ -83,6 +107,8 @@ _SIGS = {
                                 ctypes.c_size_t, _P, _P, _P, _P, _P]),
     "kara_attention_workspace_bytes": (ctypes.c_size_t, [_P, _I, _I]),
     "kara_decode_attention": (_I, [_P, _I, _I, _P, _P, _I, _P, _I, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "kara_sim_gen_length": (_I, [_P, _I]),
+    "kara_policy_sim": (_I, [_P, _P, _P, _P, _P]),
 }
 EXPORTED = tuple(_SIGS)
 
@@ -333,3 +359,36 @@ def kara_decode_attention(shape, layer, q, kv_pool, block_table_d, seq_lens_h, s
         _host_i32(seq_lens_h, "seq_lens_h"), _dev(seq_lens_d, "seq_lens_d", torch.int32),
         _dev(out, "out", torch.float32), _dev(workspace, "workspace"),
         workspace.numel() * workspace.element_size() if workspace is not None else 0, _stream(stream)))
+
+
+def _sim_config(cfg):
+    c = kara_sim_config()
+    for name, _ in kara_sim_config._fields_:
+        if name == "policy":
+            c.policy = _POLICIES[cfg["policy"]]
+        else:
+            setattr(c, name, cfg.get(name, 0))
+    return c
+
+
+def kara_sim_gen_length(cfg, request):
+    c = _sim_config(cfg)
+    return int(_lib.kara_sim_gen_length(ctypes.byref(c), int(request)))
+
+
+def kara_policy_sim(cfg):
+    """Host-only serving-policy simulation (see include/kara.h).  cfg: dict
+    with the kara_sim_config fields, policy "periodic" or "threshold".
+    Returns (summary dict, list of (running, compressions, ms) per step)."""
+    c = _sim_config(cfg)
+    r = kara_sim_result()
+    n = max(int(cfg["max_steps"]), 1)
+    act = (ctypes.c_int32 * n)()
+    comp = (ctypes.c_int32 * n)()
+    ms = (ctypes.c_double * n)()
+    st = _lib.kara_policy_sim(ctypes.byref(c), ctypes.byref(r), act, comp, ms)
+    if st != KARA_OK:
+        raise KaraError(st, "kara_policy_sim: inconsistent settings")
+    summary = {name: getattr(r, name) for name, _ in kara_sim_result._fields_}
+    steps = [(act[i], comp[i], ms[i]) for i in range(r.steps)]
+    return summary, steps

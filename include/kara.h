@@ -344,6 +344,69 @@ kara_status kara_schedule_step(int64_t step, int32_t period, int32_t window, int
                                const int32_t* seq_lens, const int32_t* watermarks,
                                const uint8_t* selected, int32_t* batch_out, int32_t* n_batch);
 
+/* ------------------------------------------------------------------------
+ * Serving-policy simulator (host only).  Periodic window compression against
+ * threshold-triggered whole-cache compression under a KV memory cap and a
+ * concurrency limit ("Technical Summary: Kara", Problem Statement 1:
+ * threshold triggering lowers throughput as concurrency grows; Methodology
+ * 3: the periodic policy; paper, Fig. 1 caption: compression frees memory so
+ * more sequences decode at once).  Per-step costs are inputs (measured kernel
+ * timings); the rules of a step are, in order:
+ *   1. admission: waiting requests enter in order while fewer than max_batch
+ *      run and the pool holds the prompt's blocks plus one spare block;
+ *   2. decode: each running sequence, in admission order, appends one token,
+ *      taking a new block when its length is a multiple of block_size (with
+ *      no free block it stalls for the step); if all of them stalled, the
+ *      most recently admitted one is preempted: its blocks are freed and it
+ *      returns to the front of the queue to restart from its prompt;
+ *   3. sequences that generated all their tokens leave and free their blocks;
+ *   4. compression: periodic - at multiples of `period`, every running
+ *      sequence with length - watermark >= window goes from L to
+ *      L - (window - protect) + budget tokens, its tail from block
+ *      (L - window) / bs on rewritten into ceil(((L - window) mod bs + budget
+ *      + protect) / bs) blocks, watermark = new length - protect;
+ *      threshold - every running sequence with length >= threshold keeps
+ *      `keep` tokens (ceil(keep / bs) blocks);
+ *   5. step time = decode_ms_fixed + decode_ms_per_token * (cached tokens of
+ *      the sequences running at the start of step 2) + compression cost
+ *      (periodic: compress_ms_per_seq per sequence; threshold:
+ *      compress_ms_per_key times the sequence's length).
+ * Request i generates kara_sim_gen_length(config, i) tokens: gen_min +
+ * SplitMix64(seed + i) mod (gen_max - gen_min + 1).
+ * ------------------------------------------------------------------------ */
+
+enum { KARA_POLICY_PERIODIC = 0, KARA_POLICY_THRESHOLD = 1, KARA_POLICY_NONE = 2 /* no compression */ };
+
+typedef struct {
+  int32_t policy;              /* KARA_POLICY_* */
+  int32_t n_requests, max_batch, cap_blocks, block_size;
+  int32_t prompt_len, gen_min, gen_max;
+  uint64_t seed;
+  int32_t window, protect, budget, period;   /* periodic */
+  int32_t threshold, keep;                    /* threshold */
+  double decode_ms_fixed, decode_ms_per_token;
+  double compress_ms_per_seq, compress_ms_per_key;
+  int32_t max_steps;
+} kara_sim_config;
+
+typedef struct {
+  int64_t steps, tokens, compressions, stalls, peak_blocks;
+  int64_t preemptions, wasted;  /* restarts, and tokens generated before them */
+  int32_t finished;            /* requests that generated all their tokens */
+  double total_ms, compress_ms, mean_active;
+} kara_sim_result;
+
+/* Tokens request `request` generates (see above). */
+int32_t kara_sim_gen_length(const kara_sim_config* config, int32_t request);
+
+/* Runs the simulation until every request finished or max_steps steps.
+ * Optional per-step outputs (NULL: not written), max_steps entries each:
+ * running sequences after the step, compressions in the step, step time.
+ * KARA_E_INVAL on inconsistent settings (nothing written). */
+kara_status kara_policy_sim(const kara_sim_config* config, kara_sim_result* result,
+                            int32_t* active_per_step, int32_t* compressions_per_step,
+                            double* ms_per_step);
+
 #ifdef __cplusplus
 }
 #endif
