@@ -8,8 +8,10 @@
 // the R kept window positions, then the B protected tokens.  Source blocks are
 // never written, so the copy is hazard-free and can run again on the same
 // inputs.  A row is head_dim elements (256 B for bf16 x 128); each lane moves
-// 16 B, a wave moves rows in groups, and every lane issues all its loads before
-// its stores so that several 16-B loads per lane are in flight.
+// 16 B, a wave moves rows in groups, and every lane issues all its loads (8)
+// before its stores.  The unit's kept positions and the sequence's tail block
+// ids are staged in LDS first, so a row's source and destination addresses
+// need no global loads.
 
 #include "kara_internal.hpp"
 
@@ -17,11 +19,16 @@ namespace kara {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
+constexpr int kUnroll = 8;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
+// Table entries a unit can touch: the tail from the boundary block, at most
+// ceil((W + bs - 1) / bs) blocks, old or new.
+__host__ __device__ inline int tail_blocks(int W, int bs) { return (W + bs - 1) / bs + 1; }
+
 __global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs a) {
+  extern __shared__ int32_t sh[];         // [R] kept positions, old tail ids, new tail ids
   const int cu = blockIdx.x;              // ((b * Lyr + l) * 2 + kv) * Hkv + h
   const int h = cu % a.Hkv;
   const int t1 = cu / a.Hkv;
@@ -29,6 +36,7 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs a) {
   const int bl = t1 >> 1;                 // b * Lyr + l
   const int l = bl % a.Lyr;
   const int b = bl / a.Lyr;
+  const int tid = threadIdx.x;
 
   const int W = a.W, B = a.B, R = a.R, bs = a.bs;
   const int max_tok = a.MB * bs;
@@ -39,39 +47,44 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs a) {
   const int p = start - f0 * bs;
   const int n_rows = p + R + B;
   const int C = W - B;
+  const int n_tail = tail_blocks(W, bs);
 
+  // Stage the unit's kept positions and the sequence's old and new tail block
+  // ids in LDS, so that every row copy below is one dependent global load.
+  int32_t* s_ret = sh;
+  int32_t* s_old = sh + R;
+  int32_t* s_new = s_old + n_tail;
+  auto clampb = [&](int blk) { return blk < 0 ? 0 : (blk >= a.NB ? a.NB - 1 : blk); };
   const int32_t* ret = a.retained + (size_t)bl * a.Hkv * R + (size_t)h * R;
-  const int32_t* otab = a.old_table + (size_t)b * a.MB;
-  const int32_t* ntab = a.new_table + (size_t)b * a.MB;
+  for (int i = tid; i < R; i += kThreads) {
+    const int j = ret[i];
+    s_ret[i] = j < 0 ? 0 : (j >= C ? C - 1 : j);
+  }
+  for (int i = tid; i < n_tail; i += kThreads) {
+    const int e = f0 + i < a.MB ? f0 + i : a.MB - 1;
+    s_old[i] = clampb(a.old_table[(size_t)b * a.MB + e]);
+    s_new[i] = clampb(a.new_table[(size_t)b * a.MB + e]);
+  }
+  __syncthreads();
+
   const size_t row_bytes = (size_t)a.row_bytes;
   const size_t blk_bytes = (size_t)a.Hkv * bs * row_bytes;
   char* base = (char*)a.pool + ((size_t)(l * 2 + kv) * a.NB * a.Hkv + h) * bs * row_bytes;
-
   const int pieces = a.row_bytes / 16;            // 16-B pieces per row
   const int rows_per_pass = kThreads / pieces;    // rows moved per pass of the block
-  const int my_row = threadIdx.x / pieces;
-  const int pc = threadIdx.x - my_row * pieces;
+  const int my_row = tid / pieces;
+  const int pc = tid - my_row * pieces;
   if (my_row >= rows_per_pass) return;            // lanes beyond whole rows idle (no barriers below)
 
-  auto clampb = [&](int blk) { return blk < 0 ? 0 : (blk >= a.NB ? a.NB - 1 : blk); };
+  // Row n of the new tail: the boundary block's leading tokens, the kept
+  // window positions, the protected tokens.  Token t of the old sequence lies
+  // in old tail block t / bs - f0; new row n in new tail block n / bs.
   auto src_of = [&](int n) -> const u32x4* {
-    int t;
-    if (n < p) {
-      t = f0 * bs + n;
-    } else if (n < p + R) {
-      int j = ret[n - p];
-      j = j < 0 ? 0 : (j >= C ? C - 1 : j);
-      t = start + j;
-    } else {
-      t = L - B + (n - p - R);
-    }
-    return (const u32x4*)(base + (size_t)clampb(otab[t / bs]) * blk_bytes + (size_t)(t % bs) * row_bytes) + pc;
+    const int t = n < p ? f0 * bs + n : (n < p + R ? start + s_ret[n - p] : L - B + (n - p - R));
+    return (const u32x4*)(base + (size_t)s_old[t / bs - f0] * blk_bytes + (size_t)(t % bs) * row_bytes) + pc;
   };
   auto dst_of = [&](int n) -> u32x4* {
-    const int pos = f0 * bs + n;                  // token position in the new sequence
-    int e = pos / bs;
-    e = e >= a.MB ? a.MB - 1 : e;
-    return (u32x4*)(base + (size_t)clampb(ntab[e]) * blk_bytes + (size_t)(pos % bs) * row_bytes) + pc;
+    return (u32x4*)(base + (size_t)s_new[n / bs] * blk_bytes + (size_t)(n % bs) * row_bytes) + pc;
   };
 
   for (int n0 = my_row; n0 < n_rows; n0 += rows_per_pass * kUnroll) {
@@ -94,7 +107,8 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs a) {
 hipError_t launch_compact(const CompactArgs& a, hipStream_t stream) {
   const long long n = (long long)a.S * a.Lyr * 2 * a.Hkv;
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(compact_kernel, dim3((unsigned)n), dim3(kThreads), 0, stream, a);
+  const size_t lds = ((size_t)a.R + 2 * (size_t)tail_blocks(a.W, a.bs)) * sizeof(int32_t);
+  hipLaunchKernelGGL(compact_kernel, dim3((unsigned)n), dim3(kThreads), lds, stream, a);
   return hipGetLastError();
 }
 

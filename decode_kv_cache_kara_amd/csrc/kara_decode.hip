@@ -12,17 +12,21 @@
 //   the compressed cache is served through PagedAttention).  It is bound by
 //   HBM: per token and KV head it reads one K and one V row (2 * D * elt
 //   bytes) and does 4 * G * D flops.  Layout of the work:
-//     * a workgroup takes 256 tokens of one (sequence, KV head) ("split");
-//       the G query heads of the group share every K/V row it reads;
+//     * a workgroup takes 512 tokens of one (sequence, KV head) ("split");
+//       the G query heads of the group share every K/V row it reads, and the
+//       split's block ids are staged in LDS first;
 //     * 16 lanes hold one token's row as 16-byte pieces, so a wave loads 4
 //       tokens' rows per instruction, fully coalesced within a block row;
-//     * each lane group takes 4 tokens per step (8 loads in flight per lane),
-//       reduces the G dot products across its 16 lanes, and updates a running
-//       maximum, sum and output with one rescale per step;
+//     * each lane group takes 4 tokens per step (8 loads in flight per lane);
+//       bf16 dot products use the packed bf16 dot instruction (two products
+//       per instruction, no unpacking of K) and are summed across the 16
+//       lanes with DPP row permutations;
+//     * a running maximum, sum and output per query head are rescaled only
+//       when some lane's maximum moves;
 //     * lane groups, waves and then splits are merged with the usual
 //       (max, sum, output) rescaling; the split merge is a second kernel.
-//   Logits are kept in log2 units: the queries are pre-multiplied by
-//   log2(e) / sqrt(D) and exp2 is used throughout.
+//   Logits are kept in log2 units (the dot products are scaled by
+//   log2(e) / sqrt(D)) and exp2 is used throughout.
 
 #include "kara_internal.hpp"
 
@@ -82,7 +86,9 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
 
 constexpr int kAttnThreads = 256;
 constexpr int kAttnWaves = kAttnThreads / 64;
-constexpr int kU = 4;  // tokens per lane group per step
+// Tokens per lane group per step.  Fetching the next step's rows ahead of the
+// current step's arithmetic costs occupancy and measured slower.
+constexpr int kU = 4;
 
 template <typename T>
 __device__ __forceinline__ void unpack(const u32x4& w, float* f);
@@ -114,14 +120,37 @@ __device__ __forceinline__ void merge(float& m, float& l, float* o, float m2, fl
   m = mn;
 }
 
+template <int Ctrl>
+__device__ __forceinline__ float dpp_add(float x) {
+  return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), Ctrl, 0xF, 0xF,
+                                                                   false));
+}
+
+// Sum over aligned groups of N lanes (N = 2 .. 32), every lane of a group
+// receiving the group's sum: swaps within quads, then the mirrored quad of
+// the half row, then the mirrored half row (DPP), then the other row.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  x = dpp_add<0xB1>(x);                      // quad_perm [1,0,3,2]
+  if constexpr (N >= 4) x = dpp_add<0x4E>(x);   // quad_perm [2,3,0,1]
+  if constexpr (N >= 8) x = dpp_add<0x141>(x);  // row_half_mirror
+  if constexpr (N >= 16) x = dpp_add<0x140>(x); // row_mirror
+  if constexpr (N >= 32) x += __shfl_xor(x, 16);
+  return x;
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
 template <typename T, int D, int G>
 __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
   constexpr int E = 16 / (int)sizeof(T);        // elements per 16-byte piece
   constexpr int kLanes = D / E;                 // lanes per token row
   constexpr int kGroups = 64 / kLanes;          // tokens per wave per load
   constexpr int kRowBytes = D * (int)sizeof(T);
+  constexpr bool kBf16 = sizeof(T) == 2;
   __shared__ float sh_m[kAttnWaves][G], sh_l[kAttnWaves][G];
   __shared__ float sh_o[kAttnWaves][G][D];
+  __shared__ int32_t sh_blk[kAttnChunk + 1];
 
   const int split = blockIdx.x % a.n_split;
   const int h = (blockIdx.x / a.n_split) % a.Hkv;
@@ -135,16 +164,21 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
   const int t0 = split * kAttnChunk;
   const int t1 = min(L, t0 + kAttnChunk);
 
-  // this lane's piece of the G query rows, in log2 units
-  float q[G][E];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const u32x4 w = *(const u32x4*)((const char*)a.q +
-                                    (((size_t)b * a.Hq + h * G + g) * D + sub * E) * sizeof(T));
-    unpack<T>(w, q[g]);
-#pragma unroll
-    for (int e = 0; e < E; ++e) q[g][e] *= a.c;
+  // the split's block ids, clamped to the pool
+  const int e0 = t0 / a.bs;
+  const int n_e = t1 > t0 ? (t1 - 1) / a.bs - e0 + 1 : 0;
+  for (int i = tid; i < n_e; i += kAttnThreads) {
+    const int blk = a.table[(size_t)b * a.MB + e0 + i];
+    sh_blk[i] = blk < 0 ? 0 : (blk >= a.NB ? a.NB - 1 : blk);
   }
+  __syncthreads();
+
+  // this lane's piece of the G query rows: packed bf16 pairs (bf16), or
+  // floats (fp32); logits are scaled to log2 units after the dot product
+  u32x4 qw[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+    qw[g] = *(const u32x4*)((const char*)a.q + (((size_t)b * a.Hq + h * G + g) * D + sub * E) * sizeof(T));
   float m[G], l[G], o[G][E];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -154,45 +188,50 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
     for (int e = 0; e < E; ++e) o[g][e] = 0.0f;
   }
 
-  const int32_t* trow = a.table + (size_t)b * a.MB;
   const char* kbase = (const char*)a.pool + ((size_t)a.layer * 2 * a.NB * a.Hkv + h) * a.bs * kRowBytes;
   const size_t v_off = (size_t)a.NB * a.Hkv * a.bs * kRowBytes;
   const size_t blk_bytes = (size_t)a.Hkv * a.bs * kRowBytes;
   constexpr int kStep = kAttnWaves * kGroups * kU;   // tokens per workgroup step
+  const int my0 = (wave * kGroups + grp) * kU;
 
-  for (int base = t0 + (wave * kGroups + grp) * kU; base - (wave * kGroups + grp) * kU < t1; base += kStep) {
-    u32x4 kw[kU], vw[kU];
-    bool ok[kU];
+  auto load_rows = [&](int base, u32x4* kw, u32x4* vw) {
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const int t = base + u;
-      ok[u] = t < t1;
-      const int tc = ok[u] ? t : t1 - 1;
-      int blk = trow[tc / a.bs];
-      blk = blk < 0 ? 0 : (blk >= a.NB ? a.NB - 1 : blk);
-      const char* p = kbase + (size_t)blk * blk_bytes + (size_t)(tc % a.bs) * kRowBytes + sub * 16;
+      const int t = base + my0 + u;
+      const int tc = t < t1 ? t : t1 - 1;
+      const char* p = kbase + (size_t)sh_blk[tc / a.bs - e0] * blk_bytes + (size_t)(tc % a.bs) * kRowBytes + sub * 16;
       kw[u] = __builtin_nontemporal_load((const u32x4*)p);
       vw[u] = __builtin_nontemporal_load((const u32x4*)(p + v_off));
     }
+  };
+  for (int base = t0; base < t1; base += kStep) {
+    u32x4 kw[kU], vw[kU];
+    bool ok[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) ok[u] = base + my0 + u < t1;
+    load_rows(base, kw, vw);
     float x[kU][G];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      float kf[E];
-      unpack<T>(kw[u], kf);
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         float d = 0.0f;
+        if constexpr (kBf16) {
+          // (A bit cast of an indexed vector element inside this unrolled
+          // loop compiles to element 0 every time with the ROCm 7.2 clang;
+          // copying the pairs out first is compiled correctly.)
+          bf16x2 qp[4], kp[4];
+          __builtin_memcpy(qp, &qw[g], 16);
+          __builtin_memcpy(kp, &kw[u], 16);
 #pragma unroll
-        for (int e = 0; e < E; ++e) d = fmaf(q[g][e], kf[e], d);
-        x[u][g] = d;
+          for (int i = 0; i < 4; ++i) d = __builtin_amdgcn_fdot2_f32_bf16(qp[i], kp[i], d, false);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) d = fmaf(__uint_as_float(qw[g][i]), __uint_as_float(kw[u][i]), d);
+        }
+        x[u][g] = group_sum<kLanes>(d) * a.c;
       }
     }
-#pragma unroll
-    for (int off = kLanes / 2; off >= 1; off >>= 1)
-#pragma unroll
-      for (int u = 0; u < kU; ++u)
-#pragma unroll
-        for (int g = 0; g < G; ++g) x[u][g] += __shfl_xor(x[u][g], off);
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       float mx = m[g];
@@ -201,12 +240,15 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
         if (!ok[u]) x[u][g] = -INFINITY;
         mx = fmaxf(mx, x[u][g]);
       }
-      if (mx == -INFINITY) continue;              // nothing seen yet in this lane group
-      const float sc = __builtin_amdgcn_exp2f(m[g] - mx);
-      l[g] *= sc;
+      // rescale only when some lane's running maximum moves (rare after the
+      // first tokens); lanes whose maximum did not move multiply by 1
+      if (__ballot(mx > m[g])) {
+        const float sc = (mx == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m[g] - mx);
+        l[g] *= sc;
 #pragma unroll
-      for (int e = 0; e < E; ++e) o[g][e] *= sc;
-      m[g] = mx;
+        for (int e = 0; e < E; ++e) o[g][e] *= sc;
+        m[g] = mx;
+      }
     }
 #pragma unroll
     for (int u = 0; u < kU; ++u) {

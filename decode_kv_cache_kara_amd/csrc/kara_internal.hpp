@@ -73,8 +73,9 @@ struct AppendArgs {
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 
-// Tokens of one (sequence, KV head) per decode-attention workgroup.
-constexpr int kAttnChunk = 256;
+// Tokens of one (sequence, KV head) per decode-attention workgroup (512 beat
+// 128, 256, 1024 and 2048 at the Qwen3-4B-shaped compacted cache).
+constexpr int kAttnChunk = 512;
 
 struct AttnArgs {
   const void* q;              // [S][Hq][D]

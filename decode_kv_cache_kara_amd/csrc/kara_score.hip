@@ -71,7 +71,11 @@ constexpr int kRT = 1;
 constexpr int kRowsPerWave = 32 * kRT;
 constexpr int kWaves = kScoreRowsPerChunk / kRowsPerWave;
 constexpr int kThreads = kWaves * 64;
+// Keys per LDS tile, one barrier each.  128-key tiles halve the barriers but
+// need a second staging register set (spills at 128 VGPRs) and measured
+// slower on gfx950.
 constexpr int kKeyTile = 64;
+constexpr int kSub = kKeyTile / 32;               // 32-key subtiles per tile
 
 template <typename T>
 struct Mma;
@@ -238,7 +242,7 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerEU) void score_kernel(ScoreAr
   // LDS holds three key tiles: the two being multiplied and the one being
   // filled.
   typedef f32x16 Acc[kRT];
-  Acc accA, accB;
+  Acc acc[2];   // subtile s is multiplied into acc[s & 1]
   auto mma_sub = [&](Acc& acc, int buf, int kt, auto keys_on_m) {
 #pragma unroll
     for (int qt = 0; qt < kRT; ++qt) {
@@ -337,26 +341,28 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerEU) void score_kernel(ScoreAr
     T2 = min(C - 1, i_last) / kKeyTile + 1;
   }
   prologue(T1);
-  mma_sub(accA, 0, 0, std::true_type());
+  mma_sub(acc[0], 0, 0, std::true_type());
   for (int t = 0; t + 1 < T1; ++t) {
-    const int b0 = t % 3, b1 = (t + 1) % 3, b2 = (t + 2) % 3;
-    mma_sub(accB, b0, 1, std::true_type());
-    stats_sub(accA, t * kKeyTile, std::false_type());
-    interleave();
-    pin();
-    mma_sub(accA, b1, 0, std::true_type());
-    stats_sub(accB, t * kKeyTile + 32, std::false_type());
-    interleave();
-    pin();
-    store_tile(stage0, b2);
+    const int bt = t % 3, bn = (t + 1) % 3;
+#pragma unroll
+    for (int k = 0; k < kSub; ++k) {
+      if (k + 1 < kSub) mma_sub(acc[(k + 1) & 1], bt, k + 1, std::true_type());
+      else mma_sub(acc[0], bn, 0, std::true_type());
+      stats_sub(acc[k & 1], t * kKeyTile + 32 * k, std::false_type());
+      interleave();
+      pin();
+    }
+    store_tile(stage0, (t + 2) % 3);
     __syncthreads();
     load_tile(stage0, (t + 3 < T1 ? t + 3 : T1 - 1) * kKeyTile);
   }
   {
-    const int t = T1 - 1;
-    mma_sub(accB, t % 3, 1, std::true_type());
-    stats_sub(accA, t * kKeyTile, std::true_type());
-    stats_sub(accB, t * kKeyTile + 32, std::true_type());
+    const int t = T1 - 1, bt = t % 3;
+#pragma unroll
+    for (int k = 0; k < kSub; ++k) {
+      if (k + 1 < kSub) mma_sub(acc[(k + 1) & 1], bt, k + 1, std::true_type());
+      stats_sub(acc[k & 1], t * kKeyTile + 32 * k, std::true_type());
+    }
   }
   __syncthreads();
 
@@ -414,35 +420,39 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerEU) void score_kernel(ScoreAr
     if (lane < 32) col_ring[t & 1][wave][kt * 32 + lane] = col;
   };
   auto flush_cols = [&](int t) {
-    const int key = t * kKeyTile + lane;
-    if (wave == 0 && key < C) {
+    // waves 0 .. kKeyTile/64 - 1 each add up 64 keys' per-wave partials
+    const int key = t * kKeyTile + wave * 64 + lane;
+    if (wave < kKeyTile / 64 && key < C) {
       float sum = 0.0f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) sum += col_ring[t & 1][w][lane];
+      for (int w = 0; w < kWaves; ++w) sum += col_ring[t & 1][w][wave * 64 + lane];
       out[key] = sum;
     }
   };
   prologue(T2);
-  mma_sub(accA, 0, 0, std::false_type());
+  mma_sub(acc[0], 0, 0, std::false_type());
   for (int t = 0; t + 1 < T2; ++t) {
-    const int b0 = t % 3, b1 = (t + 1) % 3, b2 = (t + 2) % 3;
+    const int bt = t % 3, bn = (t + 1) % 3;
     if (t > 0) flush_cols(t - 1);
-    mma_sub(accB, b0, 1, std::false_type());
-    col_sub(accA, t, 0);
-    interleave();
-    mma_sub(accA, b1, 0, std::false_type());
-    col_sub(accB, t, 1);
-    interleave();
-    store_tile(stage0, b2);
+#pragma unroll
+    for (int k = 0; k < kSub; ++k) {
+      if (k + 1 < kSub) mma_sub(acc[(k + 1) & 1], bt, k + 1, std::false_type());
+      else mma_sub(acc[0], bn, 0, std::false_type());
+      col_sub(acc[k & 1], t, k);
+      interleave();
+    }
+    store_tile(stage0, (t + 2) % 3);
     __syncthreads();
     load_tile(stage0, (t + 3 < T2 ? t + 3 : T2 - 1) * kKeyTile);
   }
   {
-    const int t = T2 - 1;
+    const int t = T2 - 1, bt = t % 3;
     if (t > 0) flush_cols(t - 1);
-    mma_sub(accB, t % 3, 1, std::false_type());
-    col_sub(accA, t, 0);
-    col_sub(accB, t, 1);
+#pragma unroll
+    for (int k = 0; k < kSub; ++k) {
+      if (k + 1 < kSub) mma_sub(acc[(k + 1) & 1], bt, k + 1, std::false_type());
+      col_sub(acc[k & 1], t, k);
+    }
     __syncthreads();
     flush_cols(t);
   }
