@@ -132,6 +132,8 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerEU) void score_kernel(ScoreAr
   __shared__ __attribute__((aligned(16))) char kbuf[3][kKeyTile * kStride];
   __shared__ float bias_lds[kWaves * kRowsPerWave];
   __shared__ float col_ring[2][kWaves][kKeyTile];
+  __shared__ int32_t s_blk[kMaxWindow + 1];        // the window's block ids
+  __shared__ int s_redo;                            // pass 1 must run again exactly
 
   // Block -> (unit, chunk).  Consecutive block ids go to different XCDs, so
   // unit = slot-group * 8 + xcd keeps all chunks of a unit on one XCD.
@@ -198,6 +200,17 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerEU) void score_kernel(ScoreAr
 
   // Global -> register staging of key tiles: a tile is fetched one tile ahead
   // of its LDS store.  Block sizes are powers of two (bs = 1 << bs_shift).
+  // The window's block ids are staged in LDS first, so a tile's row
+  // addresses need no global loads; a thread always moves the same row piece
+  // of a tile, so only the tile offset changes between tiles.
+  const int e0 = start >> a.bs_shift;
+  const int n_e = ((start + W - 1) >> a.bs_shift) - e0 + 1;
+  if (tid == 0) s_redo = 0;
+  for (int i = tid; i < n_e; i += kThreads) {
+    const int blk = trow[e0 + i];
+    s_blk[i] = blk < 0 ? 0 : (blk >= a.NB ? a.NB - 1 : blk);
+  }
+  __syncthreads();
   typedef uint4 Stage[kPerThread];
   Stage stage0;
   const int bs_mask = (1 << a.bs_shift) - 1;
@@ -209,9 +222,8 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerEU) void score_kernel(ScoreAr
       const int j = tile0 + r;
       if (p < kTilePieces && j < W) {
         const int t = start + j;
-        int blk = trow[t >> a.bs_shift];
-        blk = blk < 0 ? 0 : (blk >= a.NB ? a.NB - 1 : blk);
-        const char* src = kbase + (size_t)blk * blk_bytes + (size_t)(t & bs_mask) * kRowBytes + pc * 16;
+        const char* src = kbase + (size_t)s_blk[(t >> a.bs_shift) - e0] * blk_bytes +
+                          (size_t)(t & bs_mask) * kRowBytes + pc * 16;
         st[u] = *(const uint4*)src;
       } else {
         st[u] = make_uint4(0u, 0u, 0u, 0u);
@@ -283,11 +295,7 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerEU) void score_kernel(ScoreAr
   // the wave (subtiles whose last key is past it cross the diagonal).
   int i_lane[kRT];
 #pragma unroll
-  for (int qt = 0; qt < kRT; ++qt) {
-    m_run[qt] = -INFINITY;
-    l_run[qt] = 0.0f;
-    i_lane[qt] = (row0 + qt * 32 + (lane & 31)) / G;
-  }
+  for (int qt = 0; qt < kRT; ++qt) i_lane[qt] = (row0 + qt * 32 + (lane & 31)) / G;
   const int i_wave = row0 / G;
   // Keeps a step's VALU results ahead of the point that follows (the compiler
   // would otherwise sink the exponentials past the next barrier, away from the
@@ -296,7 +304,17 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerEU) void score_kernel(ScoreAr
 #pragma unroll
     for (int qt = 0; qt < kRT; ++qt) asm volatile("" ::"v"(m_run[qt]), "v"(l_run[qt]));
   };
-  auto stats_sub = [&](Acc& accs, int key0, auto masked) {
+  // Two ways to accumulate the row statistics.  Exact: a running maximum,
+  // updated every subtile, with the sum rescaled when it moves.  Fixed
+  // reference (the method's scoring, not the unidirectional ablation): the
+  // maximum of the lane's first 16 keys is the reference for the whole row, so
+  // every later subtile costs one multiply-add, one exp2 and one add per
+  // logit.  The sum is then exact in the same way (it is scaled by a power of
+  // two fixed per row) unless a later logit exceeds the reference by more
+  // than the float range allows (about 88 nats) or the lane saw no key in its
+  // first subtile; then the whole workgroup runs pass 1 again exactly.
+  float mc_fix[kRT];
+  auto stats_sub = [&](Acc& accs, int key0, auto masked, auto exact, bool first) {
 #pragma unroll
     for (int qt = 0; qt < kRT; ++qt) {
       f32x16& acc = accs[qt];
@@ -313,21 +331,30 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerEU) void score_kernel(ScoreAr
         for (int r = 0; r < 16; ++r)
           if (key0 + acc_row(r, lane) >= W) acc[r] = -INFINITY;
       }
-      float m0 = fmaxf(acc[0], acc[1]), m1 = fmaxf(acc[8], acc[9]);
+      float mc;
+      if (decltype(exact)::value || first) {
+        float m0 = fmaxf(acc[0], acc[1]), m1 = fmaxf(acc[8], acc[9]);
 #pragma unroll
-      for (int r = 2; r < 8; ++r) {
-        m0 = fmaxf(m0, acc[r]);
-        m1 = fmaxf(m1, acc[8 + r]);
+        for (int r = 2; r < 8; ++r) {
+          m0 = fmaxf(m0, acc[r]);
+          m1 = fmaxf(m1, acc[8 + r]);
+        }
+        const float mx = fmaxf(fmaxf(m0, m1), m_run[qt]);
+        // Only a masked subtile can leave a lane with no key seen so far.
+        mc = mx * c;
+        if (kUni || decltype(masked)::value) mc = (mx == -INFINITY) ? 0.0f : mc;
+        if (!decltype(exact)::value) mc_fix[qt] = mc;
+        l_run[qt] *= fast_exp2(m_run[qt] * c - mc);
+        m_run[qt] = mx;
+      } else {
+        mc = mc_fix[qt];
       }
-      const float mx = fmaxf(fmaxf(m0, m1), m_run[qt]);
-      // Only a masked subtile can leave a lane with no key seen so far.
-      float mc = mx * c;
-      if (kUni || decltype(masked)::value) mc = (mx == -INFINITY) ? 0.0f : mc;
-      float sp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      float sp[4];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sp[r & 3] += fast_exp2(fmaf(acc[r], c, -mc));
-      l_run[qt] = l_run[qt] * fast_exp2(m_run[qt] * c - mc) + ((sp[0] + sp[1]) + (sp[2] + sp[3]));
-      m_run[qt] = mx;
+      for (int r = 0; r < 4; ++r) sp[r] = fast_exp2(fmaf(acc[r], c, -mc));
+#pragma unroll
+      for (int r = 4; r < 16; ++r) sp[r & 3] += fast_exp2(fmaf(acc[r], c, -mc));
+      l_run[qt] += (sp[0] + sp[1]) + (sp[2] + sp[3]);
     }
   };
   // Key tiles: all of the window, or (unidirectional) up to the tile holding
@@ -340,31 +367,52 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerEU) void score_kernel(ScoreAr
     T1 = i_last / kKeyTile + 1;
     T2 = min(C - 1, i_last) / kKeyTile + 1;
   }
-  prologue(T1);
-  mma_sub(acc[0], 0, 0, std::true_type());
-  for (int t = 0; t + 1 < T1; ++t) {
-    const int bt = t % 3, bn = (t + 1) % 3;
+  auto pass1 = [&](auto exact) {
 #pragma unroll
-    for (int k = 0; k < kSub; ++k) {
-      if (k + 1 < kSub) mma_sub(acc[(k + 1) & 1], bt, k + 1, std::true_type());
-      else mma_sub(acc[0], bn, 0, std::true_type());
-      stats_sub(acc[k & 1], t * kKeyTile + 32 * k, std::false_type());
-      interleave();
-      pin();
+    for (int qt = 0; qt < kRT; ++qt) {
+      m_run[qt] = -INFINITY;
+      l_run[qt] = 0.0f;
     }
-    store_tile(stage0, (t + 2) % 3);
+    prologue(T1);
+    mma_sub(acc[0], 0, 0, std::true_type());
+    for (int t = 0; t + 1 < T1; ++t) {
+      const int bt = t % 3, bn = (t + 1) % 3;
+#pragma unroll
+      for (int k = 0; k < kSub; ++k) {
+        if (k + 1 < kSub) mma_sub(acc[(k + 1) & 1], bt, k + 1, std::true_type());
+        else mma_sub(acc[0], bn, 0, std::true_type());
+        stats_sub(acc[k & 1], t * kKeyTile + 32 * k, std::false_type(), exact, t == 0 && k == 0);
+        interleave();
+        pin();
+      }
+      store_tile(stage0, (t + 2) % 3);
+      __syncthreads();
+      load_tile(stage0, (t + 3 < T1 ? t + 3 : T1 - 1) * kKeyTile);
+    }
+    {
+      const int t = T1 - 1, bt = t % 3;
+#pragma unroll
+      for (int k = 0; k < kSub; ++k) {
+        if (k + 1 < kSub) mma_sub(acc[(k + 1) & 1], bt, k + 1, std::true_type());
+        stats_sub(acc[k & 1], t * kKeyTile + 32 * k, std::true_type(), exact, t == 0 && k == 0);
+      }
+    }
+  };
+  if constexpr (kUni) {
+    pass1(std::true_type());
     __syncthreads();
-    load_tile(stage0, (t + 3 < T1 ? t + 3 : T1 - 1) * kKeyTile);
-  }
-  {
-    const int t = T1 - 1, bt = t % 3;
+  } else {
+    pass1(std::false_type());
+    bool bad = false;
 #pragma unroll
-    for (int k = 0; k < kSub; ++k) {
-      if (k + 1 < kSub) mma_sub(acc[(k + 1) & 1], bt, k + 1, std::true_type());
-      stats_sub(acc[k & 1], t * kKeyTile + 32 * k, std::true_type());
+    for (int qt = 0; qt < kRT; ++qt) bad = bad || !(l_run[qt] < INFINITY) || m_run[qt] == -INFINITY;
+    if (__ballot(bad) && lane == 0) s_redo = 1;
+    __syncthreads();
+    if (s_redo) {                                   // uniform over the workgroup
+      pass1(std::true_type());
+      __syncthreads();
     }
   }
-  __syncthreads();
 
   // Merge the two lane halves (same query, disjoint keys) and publish the row
   // bias  m*c + log2(sum)  so that  p = exp2(x*c - bias).
@@ -411,7 +459,11 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerEU) void score_kernel(ScoreAr
     }
     if (plain) {
 #pragma unroll
-      for (int qt = 0; qt < kRT; ++qt)
+      for (int r = 0; r < 4; ++r) sp[r] = fast_exp2(fmaf(accs[0][r], c, nbias[0][r]));
+#pragma unroll
+      for (int r = 4; r < 16; ++r) sp[r & 3] += fast_exp2(fmaf(accs[0][r], c, nbias[0][r]));
+#pragma unroll
+      for (int qt = 1; qt < kRT; ++qt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) sp[r & 3] += fast_exp2(fmaf(accs[qt][r], c, nbias[qt][r]));
     }

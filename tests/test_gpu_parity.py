@@ -74,6 +74,33 @@ def test_score_stage(name):
     say(name, "max rel err", worst)
 
 
+def test_score_stage_exact_fallback():
+    """One key made ~110 nats more attractive to one query than that query's
+    first keys: with the first keys' maximum as the row's reference the sum
+    would overflow float, so the workgroup must redo its row statistics with a
+    running maximum.  The scores still match the oracle."""
+    say("score stage exact fallback")
+    wl = gpu_workload(None, n_seqs=2, n_layers=1, n_q_heads=8, n_kv_heads=2, head_dim=128, block_size=16,
+                      window=256, protect=32, top_k=8, budget=40, lens=[300, 700], dtype=torch.bfloat16,
+                      qk_std=0.1)
+    b, i, j = 0, 150, 200                      # sequence, query position, key position (window-local)
+    q = wl.q_window[b, 0, i, 0].float()        # query head 0 belongs to KV head 0
+    s = 110.0 * math.sqrt(128) / float(q @ q)
+    L = int(wl.lens[b])
+    t = L - wl.window + j
+    blk = int(wl.table[b, t // wl.block_size])
+    wl.pool[0, 0, blk, 0, t % wl.block_size] = (q * s).to(torch.bfloat16)
+    kq = wl.pool[0, 0, blk, 0, t % wl.block_size].float()
+    assert float(q @ kq) / math.sqrt(128) > 100.0
+    ses = runner.Session(wl)
+    out = torch.full((wl.n_units, wl.region), float("nan"), device="cuda")
+    ses.score(out)
+    torch.cuda.synchronize()
+    orc = oracle_scores(wl).reshape(wl.n_units, wl.region)
+    assert_scores_close(out.cpu().numpy(), orc)
+    assert orc[0, j] > 0.9                     # the planted key took that row's whole weight
+
+
 REGIONS = [1, 7, 56, 187, 896, 1792, 2048]
 
 
