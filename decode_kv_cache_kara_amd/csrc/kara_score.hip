@@ -21,21 +21,22 @@
 // buffered, with a 16-byte row pad so the per-lane 16-byte reads do not
 // collide on banks.
 //
-// Per logit, pass 1 needs a max, an FMA, an exp2 and an add and pass 2 an FMA,
-// an exp2 and an add, against 2*D MFMA flops; on gfx950 v_exp_f32 costs about
-// four FMAs, so the VALU work (about 8.5 ms at the Qwen3-4B 36-layer batch of
-// 32) is as large as the MFMA work (about 7.7 ms), and the two overlap only
-// partially on one SIMD (about 30% of the shorter in microbenchmarks).  The
-// schedule therefore aims at a dense instruction stream rather than at hiding
-// one unit under the other:
-//   * each wave owns 32 rows (at most 128 VGPRs, four waves per SIMD) and
+// Per logit, pass 1 needs an FMA, an exp2 and an add (its row maximum is
+// taken once, from the first keys, see below) and pass 2 an FMA, an exp2 and
+// an add, against 2*D MFMA flops.  On gfx950 v_exp_f32 occupies the VALU
+// issue for about three FMAs and does not co-issue with other VALU work, so
+// the VALU stream (about 11-13 ms at the Qwen3-4B 36-layer batch of 32) is
+// longer than the MFMA stream (about 8 ms); the schedule keeps the VALU
+// stream dense and hides the MFMAs under it:
+//   * each wave owns 64 rows (two 32-row query tiles sharing every K
+//     fragment read from LDS; at most 256 VGPRs, two waves per SIMD) and
 //     software-pipelines over 32-key subtiles: the MFMAs of the next subtile
 //     are issued between the exponentials of the current one (scheduling
 //     groups below), so no wave waits for its own matrix results;
 //   * LDS holds three 64-key tiles (two being multiplied, one being filled),
-//     so there is one barrier per tile; sums and maxima use independent
-//     partial chains.
-//
+//     so there is one barrier per tile; the window's block ids are staged in
+//     LDS once; sums use independent partial chains.
+
 // Unidirectional ablation ("Technical Summary: Kara", Experimental Results,
 // Ablation Studies): window query i sees keys j <= i only.  A workgroup then
 // stops at the key tile that holds its last row's position, subtiles that
@@ -64,10 +65,11 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// 32-row query tiles per wave.  Two tiles halve the LDS fragment reads but
-// need 256 VGPRs (two waves per SIMD); on gfx950 one tile at four waves per
-// SIMD is as fast, so one it is.
-constexpr int kRT = 1;
+// 32-row query tiles per wave.  Two tiles let every K fragment read from LDS
+// feed two MFMAs and leave room in 256 VGPRs (two waves per SIMD) for the
+// compiler to keep fragment reads ahead of their MFMAs; measured 3% faster
+// than one tile at four waves per SIMD.
+constexpr int kRT = 2;
 constexpr int kRowsPerWave = 32 * kRT;
 constexpr int kWaves = kScoreRowsPerChunk / kRowsPerWave;
 constexpr int kThreads = kWaves * 64;
@@ -115,8 +117,9 @@ __device__ __forceinline__ int acc_row(int r, int lane) {
   return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 }
 
-// At most 128 VGPRs per wave: four waves share each SIMD.
-constexpr int kMinWavesPerEU = 4;
+// One row tile: at most 128 VGPRs (four waves per SIMD); two: at most 256
+// (two waves per SIMD).
+constexpr int kMinWavesPerEU = kRT == 1 ? 4 : 2;
 
 template <typename T, int D, bool kUni>
 __global__ __launch_bounds__(kThreads, kMinWavesPerEU) void score_kernel(ScoreArgs a) {
