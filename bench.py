@@ -51,7 +51,7 @@ def read_traffic(workload):
         return None
     with open(path) as f:
         d = json.load(f)
-    if d.get("source_sha256_16") != kernel_source_hash("kara_score.hip"):
+    if d.get("source_sha256_16") != kernel_source_hash("kara_score_kernel.hpp"):
         return None
     return d.get("hbm_bytes_per_launch")
 
