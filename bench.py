@@ -361,7 +361,7 @@ def main():
     out["decode_attention"] = decode_attention_roofline(ses, wl)
     log(f"decode attention over the compacted cache: {out['decode_attention']['ms_per_launch']:.3f} ms/layer, "
         f"{out['decode_attention']['achieved']:.0f} GB/s")
-    if args.flags == 0:
+    if args.flags == 0 and args.config == 2:       # costs scaled from the Qwen3-4B-shaped slice
         out["policy_sim"] = policy_sim(out, wl)
     if not args.no_cpu_baseline:
         del ses, wl
