@@ -309,6 +309,7 @@ def main():
         for i in range(3):
             stage[i] += ev[i].elapsed_time(ev[i + 1])
     stage = [x / args.steps for x in stage]
+    per_step = sorted(ev[0].elapsed_time(ev[3]) for ev in step_events)
     log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step; score {stage[0]:.3f} ms, "
         f"select {stage[1]:.3f} ms, compact {stage[2]:.3f} ms")
 
@@ -354,6 +355,8 @@ def main():
                      "executed_mfma_flop_per_launch": exec_flop if not uni else None},
         "stages_ms": {"score": round(stage[0], 4), "select": round(stage[1], 4),
                       "compact": round(stage[2], 4)},
+        "kernel_ms_per_step": {"median": round(per_step[len(per_step) // 2], 4), "min": round(per_step[0], 4),
+                               "max": round(per_step[-1], 4)},
         "compact_roofline": {"bound": "hbm", "kernel": "compact_kernel", "achieved": round(compact_gbs, 1),
                              "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(compact_gbs / PEAK_HBM_GBS, 4),
                              "algorithmic_bytes_per_launch": compact_bytes},
