@@ -32,19 +32,46 @@ constexpr int kWaves = kThreads / 64;
 
 enum : uint8_t { kFree = 0, kCand = 1, kSpan = 2, kTopUp = 3 };
 
+// LDS of one workgroup, carved from dynamic shared memory sized by the call:
+// per position of the region its score, order key and state; per candidate
+// (or span between consecutive candidates) the candidate position, chunk
+// score, gap, rank and ranked gap; and small scratch.
 struct SelectShared {
-  float s[kMaxRegion];
-  uint32_t key[kMaxRegion];
-  uint8_t state[kMaxRegion];
-  int cand[kMaxRegion];
-  float sigma[kMaxRegion];
-  int gap[kMaxRegion];
-  int ordgap[kMaxRegion];   // gaps in rank order, then their inclusive prefix sums
-  int rank[kMaxRegion];
-  int hist[256];
-  int scan_tmp[kWaves];
-  int misc[4];
+  float* s;           // [C]
+  uint32_t* key;      // [C]
+  uint8_t* state;     // [C]
+  int* cand;          // [K]
+  float* sigma;       // [K]
+  int* gap;           // [K]
+  int* ordgap;        // [K] gaps in rank order, then their inclusive prefix sums
+  int* rank;          // [K]
+  int* hist;          // [256]
+  int* scan_tmp;      // [kWaves]
+  int* misc;          // [4]
 };
+
+__host__ __device__ inline size_t select_lds_bytes(int C, int K) {
+  const size_t c4 = (size_t)C * 4, k4 = (size_t)K * 4;
+  return 2 * c4 + ((size_t)C + 3) / 4 * 4 + 5 * k4 + (256 + kWaves + 4) * 4;
+}
+
+__device__ inline SelectShared carve(char* base, int C, int K) {
+  SelectShared sh;
+  char* p = base;
+  auto take = [&](size_t n) { char* q = p; p += (n + 3) / 4 * 4; return q; };
+  sh.s = (float*)take((size_t)C * 4);
+  sh.key = (uint32_t*)take((size_t)C * 4);
+  sh.state = (uint8_t*)take((size_t)C);
+  sh.cand = (int*)take((size_t)K * 4);
+  sh.sigma = (float*)take((size_t)K * 4);
+  sh.gap = (int*)take((size_t)K * 4);
+  sh.ordgap = (int*)take((size_t)K * 4);
+  sh.rank = (int*)take((size_t)K * 4);
+  sh.hist = (int*)take(256 * 4);
+  sh.scan_tmp = (int*)take(kWaves * 4);
+  sh.misc = (int*)take(4 * 4);
+  return sh;
+}
 
 __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f);
@@ -283,7 +310,7 @@ __device__ void token2chunk(SelectShared& sh, int C, int R) {
 
 __global__ __launch_bounds__(kThreads) void select_kernel(SelectArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  SelectShared& sh = *reinterpret_cast<SelectShared*>(smem);
+  SelectShared sh = carve(smem, a.C, a.K);
   const int unit = blockIdx.x;
   const int C = a.C, K = a.K, R = a.R;
   const int tid = threadIdx.x;
@@ -330,14 +357,9 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelectArgs a) {
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
   if (a.n_units == 0) return hipSuccess;
-  static bool configured = false;
-  const int bytes = (int)sizeof(SelectShared);
-  if (!configured) {
-    hipError_t e = hipFuncSetAttribute((const void*)select_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-    if (e != hipSuccess) return e;
-    configured = true;
-  }
+  // at most 2 * 8 KiB + 2 KiB + 5 * 8 KiB + 1 KiB (C = K = 2048): within the
+  // default 64 KiB of dynamic LDS
+  const size_t bytes = select_lds_bytes(a.C, a.K);
   hipLaunchKernelGGL(select_kernel, dim3(a.n_units), dim3(kThreads), bytes, stream, a);
   return hipGetLastError();
 }
