@@ -17,25 +17,28 @@
 //           column accumulator; lane halves and waves merge through LDS.
 // The same Q register fragments serve as the B operand of pass 1 and the A
 // operand of pass 2 (for 32x32 MFMA both operands map lane l to matrix index
-// l%32 and K-chunk l/32).  Key tiles of 64 rows are staged through LDS, double
-// buffered, with a 16-byte row pad so the per-lane 16-byte reads do not
-// collide on banks.
+// l%32 and K-chunk l/32).  Key tiles of 64 rows are staged through LDS with a
+// 16-byte row pad, so the per-lane 16-byte fragment reads do not collide on
+// banks.
 //
 // Per logit, pass 1 needs an FMA, an exp2 and an add (its row maximum is
 // taken once, from the first keys, see below) and pass 2 an FMA, an exp2 and
-// an add, against 2*D MFMA flops.  On gfx950 v_exp_f32 occupies the VALU
-// issue for about three FMAs and does not co-issue with other VALU work, so
-// the VALU stream (about 11-13 ms at the Qwen3-4B 36-layer batch of 32) is
-// longer than the MFMA stream (about 8 ms); the schedule keeps the VALU
-// stream dense and hides the MFMAs under it:
+// an add, against 2*D MFMA flops.  On gfx950 v_exp_f32 holds the VALU for
+// about 2.5 FMAs, so the VALU stream is longer than the MFMA stream; MFMA and
+// VALU work overlap well when one wave interleaves them and poorly when they
+// come from different waves of a SIMD, so every wave interleaves its own:
 //   * each wave owns 64 rows (two 32-row query tiles sharing every K
 //     fragment read from LDS; at most 256 VGPRs, two waves per SIMD) and
 //     software-pipelines over 32-key subtiles: the MFMAs of the next subtile
-//     are issued between the exponentials of the current one (scheduling
-//     groups below), so no wave waits for its own matrix results;
+//     are issued between the exponentials of the current one, in regions
+//     fenced against reordering, and K fragments are read from LDS a few
+//     regions before their MFMAs (the pipeline section below);
 //   * LDS holds three 64-key tiles (two being multiplied, one being filled),
-//     so there is one barrier per tile; the window's block ids are staged in
-//     LDS once; sums use independent partial chains.
+//     so there is one barrier per tile; the byte offsets of the window's K
+//     rows are staged in LDS once; sums use independent partial chains.
+// Under this load the chip runs below its nominal clock, limited by power,
+// so work that moves data without need (extra LDS reads, extra
+// instructions) costs time even where it fits in idle issue slots.
 
 // Unidirectional ablation ("Technical Summary: Kara", Experimental Results,
 // Ablation Studies): window query i sees keys j <= i only.  A workgroup then
@@ -148,8 +151,8 @@ __global__ __launch_bounds__(ScoreCfg<T>::kThreads, ScoreCfg<T>::kMinWavesPerEU)
 
   __shared__ __attribute__((aligned(16))) char kbuf[3][kKeyTile * kStride];
   __shared__ float bias_lds[kWaves * kRowsPerWave];
-  __shared__ float col_ring[2][kWaves][kKeyTile];
-  __shared__ int32_t s_blk[kMaxWindow + 1];        // the window's block ids
+  __shared__ float col_ring[2][kWaves][2][kKeyTile];
+  __shared__ uint64_t s_off[kMaxWindow];           // byte offsets of the window's K rows
   __shared__ int s_redo;                            // pass 1 must run again exactly
 
   // Block -> (unit, chunk).  Consecutive block ids go to different XCDs, so
@@ -197,6 +200,19 @@ __global__ __launch_bounds__(ScoreCfg<T>::kThreads, ScoreCfg<T>::kMinWavesPerEU)
   const int wave = tid >> 6;
   const int row0 = chunk * kScoreRowsPerChunk + wave * kRowsPerWave;
 
+  // Start-up order: the block table reads are issued first and the query
+  // fragment loads after them, so the K row offsets (which need only the
+  // table) are staged in LDS while the query fragments are still in flight;
+  // memory reads of a wave complete in issue order.
+  if (tid == 0) s_redo = 0;
+  constexpr int kFill = (kMaxWindow + kThreads - 1) / kThreads;
+  int blk[kFill];
+#pragma unroll
+  for (int u = 0; u < kFill; ++u) {
+    const int j = tid + u * kThreads;
+    blk[u] = j < W ? trow[(start + j) >> a.bs_shift] : 0;
+  }
+
   // Query fragments of this wave's rows, kept in registers for both passes.
   // Row r is window position r / G, head r % G of the group.
   Frag qf[kRT][NK];
@@ -216,45 +232,40 @@ __global__ __launch_bounds__(ScoreCfg<T>::kThreads, ScoreCfg<T>::kMinWavesPerEU)
   }
 
   // Global -> register staging of key tiles: a tile is fetched one tile ahead
-  // of its LDS store.  Block sizes are powers of two (bs = 1 << bs_shift).
-  // The window's block ids are staged in LDS first, so a tile's row
-  // addresses need no global loads; a thread always moves the same row piece
-  // of a tile, so only the tile offset changes between tiles.
-  const int e0 = start >> a.bs_shift;
-  const int n_e = ((start + W - 1) >> a.bs_shift) - e0 + 1;
-  if (tid == 0) s_redo = 0;
-  for (int i = tid; i < n_e; i += kThreads) {
-    const int blk = trow[e0 + i];
-    s_blk[i] = blk < 0 ? 0 : (blk >= a.NB ? a.NB - 1 : blk);
+  // of its LDS store.  The byte offset of every window row's K row (its
+  // block's place in the pool plus its place in the block) is staged in LDS
+  // once, so a row address costs one LDS read and one add; a thread always
+  // moves the same row piece of a tile.
+  {
+    const int bs_mask = (1 << a.bs_shift) - 1;
+#pragma unroll
+    for (int u = 0; u < kFill; ++u) {
+      const int j = tid + u * kThreads;
+      const int bk = blk[u] < 0 ? 0 : (blk[u] >= a.NB ? a.NB - 1 : blk[u]);
+      if (j < W) s_off[j] = (uint64_t)(uint32_t)bk * blk_bytes + (uint64_t)(((start + j) & bs_mask) * kRowBytes);
+    }
   }
   __syncthreads();
+  constexpr int kRowsPerPass = kThreads / kPiecesPerRow;
+  const int my_r = tid / kPiecesPerRow;
+  const int my_pc = tid - my_r * kPiecesPerRow;
+  const char* kpiece = kbase + my_pc * 16;
   typedef uint4 Stage[kPerThread];
   Stage stage0;
-  const int bs_mask = (1 << a.bs_shift) - 1;
   auto load_tile = [&](Stage& st, int tile0) {
 #pragma unroll
     for (int u = 0; u < kPerThread; ++u) {
-      const int p = tid + u * kThreads;
-      const int r = p / kPiecesPerRow, pc = p % kPiecesPerRow;
+      const int r = my_r + u * kRowsPerPass;
       const int j = tile0 + r;
-      if (p < kTilePieces && j < W) {
-        const int t = start + j;
-        const char* src = kbase + (size_t)s_blk[(t >> a.bs_shift) - e0] * blk_bytes +
-                          (size_t)(t & bs_mask) * kRowBytes + pc * 16;
-        st[u] = *(const uint4*)src;
-      } else {
-        st[u] = make_uint4(0u, 0u, 0u, 0u);
-      }
+      if (r < kKeyTile && j < W) st[u] = *(const uint4*)(kpiece + s_off[j]);
+      else st[u] = make_uint4(0u, 0u, 0u, 0u);
     }
   };
   auto store_tile = [&](const Stage& st, int buf) {
 #pragma unroll
     for (int u = 0; u < kPerThread; ++u) {
-      const int p = tid + u * kThreads;
-      if (p < kTilePieces) {
-        const int r = p / kPiecesPerRow, pc = p % kPiecesPerRow;
-        *(uint4*)(&kbuf[buf][r * kStride + pc * 16]) = st[u];
-      }
+      const int r = my_r + u * kRowsPerPass;
+      if (r < kKeyTile) *(uint4*)(&kbuf[buf][r * kStride + my_pc * 16]) = st[u];
     }
   };
   auto kfrag = [&](int buf, int kt, int ks) -> Frag {
@@ -262,48 +273,81 @@ __global__ __launch_bounds__(ScoreCfg<T>::kThreads, ScoreCfg<T>::kMinWavesPerEU)
                                (ks * M::kStep + (lane >> 5) * M::kPerLane) * (int)sizeof(T)];
     return *(const Frag*)p;
   };
-
-  // ---- software-pipelined schedule -----------------------------------------
-  // Within each wave the MFMAs of the next 32-key subtile are issued between
-  // the exponentials of the current one (scheduling groups below), so the
-  // matrix core and the VALU of every SIMD work at the same time.  Each key
-  // fragment read from LDS feeds the MFMAs of all kRT row tiles of the wave.
-  // LDS holds three key tiles: the two being multiplied and the one being
-  // filled.
-  typedef f32x16 Acc[kRT];
-  Acc acc[2];   // subtile s is multiplied into acc[s & 1]
-  auto mma_sub = [&](Acc& acc, int buf, int kt, auto keys_on_m) {
-#pragma unroll
-    for (int qt = 0; qt < kRT; ++qt) {
-      f32x16 z = {};
-      acc[qt] = z;
-    }
-#pragma unroll
-    for (int ks = 0; ks < NK; ++ks) {
-      const Frag kf = kfrag(buf, kt, ks);
-#pragma unroll
-      for (int qt = 0; qt < kRT; ++qt) {
-        if constexpr (decltype(keys_on_m)::value) acc[qt] = M::run(kf, qf[qt][ks], acc[qt]);
-        else acc[qt] = M::run(qf[qt][ks], kf, acc[qt]);
-      }
-    }
-  };
-  auto interleave = [&]() {
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-    for (int i = 0; i < NK; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, kRT, 0);
-      __builtin_amdgcn_sched_group_barrier(0x402, 6 * kRT, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-  };
+  // Stages the first two key tiles (both fetched before either is stored)
+  // and starts fetching the third.
   auto prologue = [&](int n_tiles) {
+    Stage stage1;
     load_tile(stage0, 0);
+    load_tile(stage1, (n_tiles > 1 ? 1 : 0) * kKeyTile);
     store_tile(stage0, 0);
-    load_tile(stage0, (n_tiles > 1 ? 1 : 0) * kKeyTile);
-    store_tile(stage0, 1);
+    store_tile(stage1, 1);
     __syncthreads();
     load_tile(stage0, (n_tiles > 2 ? 2 : n_tiles - 1) * kKeyTile);
+  };
+
+  // ---- software pipeline ---------------------------------------------------
+  // Subtile q of a pass is 32 keys: slice q % kSub of key tile q / kSub, which
+  // sits in LDS buffer (q / kSub) % 3.  Step q multiplies subtile q+1 into one
+  // register tile while the VALU turns the logits of subtile q, in the other
+  // register tile, into exponentials and sums.  A step is kRegions regions
+  // fenced against reordering; region i issues the MFMAs of K fragment group
+  // i (kPer fragments, each shared by the kRT query tiles of the wave), 1 /
+  // kRegions of the VALU work, and the LDS reads of the group kDist regions
+  // ahead, which therefore has kDist regions of work in which to arrive.
+  // Groups rotate through a ring of kRing register sets.  Reads reach at most
+  // two subtiles ahead, so they touch only the current key tile and the next,
+  // both resident (three LDS buffers: two read, one being filled; one barrier
+  // per tile).
+  constexpr int kRegions = NK < 8 ? NK : 8;
+  constexpr int kPer = NK / kRegions;
+  constexpr int kRing = kPer == 1 ? kRegions : 2;
+  constexpr int kDist = kRing / 2;
+  constexpr int kElems = kRT * 16;                  // logits per lane per subtile
+  static_assert(kSub >= 2 && kSub % 2 == 0 && kRegions % kRing == 0, "pipeline shape");
+  Frag kf[kRing][kPer];
+  typedef f32x16 Acc[kRT];
+  Acc acc[2];   // subtile q is multiplied into acc[q & 1]
+  auto fetch = [&](int g, int buf, int kt) {
+#pragma unroll
+    for (int p = 0; p < kPer; ++p) kf[g % kRing][p] = kfrag(buf, kt, g * kPer + p);
+  };
+  // One step: MFMAs of the subtile in (mbuf, mkt) into nxt when do_m, reads
+  // that run into the subtile after it (fbuf, fkt) when do_f, VALU chunk i
+  // by valu(i).
+  auto step = [&](Acc& nxt, int mbuf, int mkt, int fbuf, int fkt, bool do_m, bool do_f, auto keys_on_m,
+                  auto&& valu) {
+    if (do_m) {
+#pragma unroll
+      for (int qt = 0; qt < kRT; ++qt) {
+        f32x16 z = {};
+        nxt[qt] = z;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kRegions; ++i) {
+      if (do_m && i + kDist < kRegions) fetch(i + kDist, mbuf, mkt);
+      if (do_f && i + kDist >= kRegions) fetch(i + kDist - kRegions, fbuf, fkt);
+      if (do_m) {
+#pragma unroll
+        for (int p = 0; p < kPer; ++p) {
+          const Frag f = kf[i % kRing][p];
+#pragma unroll
+          for (int qt = 0; qt < kRT; ++qt) {
+            if constexpr (decltype(keys_on_m)::value) nxt[qt] = M::run(f, qf[qt][i * kPer + p], nxt[qt]);
+            else nxt[qt] = M::run(qf[qt][i * kPer + p], f, nxt[qt]);
+          }
+        }
+      }
+      valu(i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // Starts a pass: subtile 0 multiplied into acc[0], the first reads of
+  // subtile 1 issued.
+  auto start_pass = [&](auto keys_on_m) {
+#pragma unroll
+    for (int g = 0; g < kDist; ++g) fetch(g, 0, 0);
+    step(acc[0], 0, 0, 0, 1, true, true, keys_on_m, [](int) {});
   };
 
   // ---------------- pass 1: row max and exp-sum over all W keys -------------
@@ -314,9 +358,7 @@ __global__ __launch_bounds__(ScoreCfg<T>::kThreads, ScoreCfg<T>::kMinWavesPerEU)
 #pragma unroll
   for (int qt = 0; qt < kRT; ++qt) i_lane[qt] = (row0 + qt * 32 + (lane & 31)) / G;
   const int i_wave = row0 / G;
-  // Keeps a step's VALU results ahead of the point that follows (the compiler
-  // would otherwise sink the exponentials past the next barrier, away from the
-  // MFMAs they are meant to overlap).
+  // Keeps a step's VALU results ahead of the point that follows.
   auto pin = [&]() {
 #pragma unroll
     for (int qt = 0; qt < kRT; ++qt) asm volatile("" ::"v"(m_run[qt]), "v"(l_run[qt]));
@@ -325,53 +367,64 @@ __global__ __launch_bounds__(ScoreCfg<T>::kThreads, ScoreCfg<T>::kMinWavesPerEU)
   // updated every subtile, with the sum rescaled when it moves.  Fixed
   // reference (the method's scoring, not the unidirectional ablation): the
   // maximum of the lane's first 16 keys is the reference for the whole row, so
-  // every later subtile costs one multiply-add, one exp2 and one add per
-  // logit.  The sum is then exact in the same way (it is scaled by a power of
-  // two fixed per row) unless a later logit exceeds the reference by more
-  // than the float range allows (about 88 nats) or the lane saw no key in its
-  // first subtile; then the whole workgroup runs pass 1 again exactly.
-  float mc_fix[kRT];
-  auto stats_sub = [&](Acc& accs, int key0, auto masked, auto exact, bool first) {
+  // every subtile costs one multiply-add, one exp2 and one add per logit.  The
+  // sum is then exact in the same way (it is scaled by a power of two fixed
+  // per row) unless a later logit exceeds the reference by more than the
+  // float range allows (about 88 nats) or the lane saw no key in its first
+  // subtile; then the whole workgroup runs pass 1 again exactly.
+  float mc_fix[kRT], mcur[kRT], sp1[kRT][4];
+  auto mask_sub = [&](Acc& accs, int key0, bool tail) {
 #pragma unroll
     for (int qt = 0; qt < kRT; ++qt) {
-      f32x16& acc = accs[qt];
+      f32x16& v = accs[qt];
       if constexpr (kUni) {
         if (key0 + 31 > i_wave) {
           // key = key0 + acc_row(r, lane) is seen iff key <= i_lane
           const int lim = i_lane[qt] - key0 - 4 * (lane >> 5);
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            if (8 * (r >> 2) + (r & 3) > lim) acc[r] = -INFINITY;
+            if (8 * (r >> 2) + (r & 3) > lim) v[r] = -INFINITY;
         }
-      } else if constexpr (decltype(masked)::value) {
+      } else if (tail) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (key0 + acc_row(r, lane) >= W) acc[r] = -INFINITY;
+          if (key0 + acc_row(r, lane) >= W) v[r] = -INFINITY;
       }
-      float mc;
-      if (decltype(exact)::value || first) {
-        float m0 = fmaxf(acc[0], acc[1]), m1 = fmaxf(acc[8], acc[9]);
+    }
+  };
+  auto lane_max = [&](const f32x16& v) {
+    float m0 = fmaxf(v[0], v[1]), m1 = fmaxf(v[8], v[9]);
 #pragma unroll
-        for (int r = 2; r < 8; ++r) {
-          m0 = fmaxf(m0, acc[r]);
-          m1 = fmaxf(m1, acc[8 + r]);
+    for (int r = 2; r < 8; ++r) {
+      m0 = fmaxf(m0, v[r]);
+      m1 = fmaxf(m1, v[8 + r]);
+    }
+    return fmaxf(m0, m1);
+  };
+  // VALU chunk i of pass 1 on the subtile starting at key0.
+  auto stats_valu = [&](Acc& accs, int key0, bool tail, auto exact, int i) {
+    if (i == 0) {
+      mask_sub(accs, key0, tail);
+#pragma unroll
+      for (int qt = 0; qt < kRT; ++qt) {
+        if constexpr (decltype(exact)::value) {
+          const float mx = fmaxf(lane_max(accs[qt]), m_run[qt]);
+          const float mc = (mx == -INFINITY) ? 0.0f : mx * c;
+          l_run[qt] *= fast_exp2(m_run[qt] * c - mc);
+          m_run[qt] = mx;
+          mcur[qt] = mc;
+        } else {
+          mcur[qt] = mc_fix[qt];
         }
-        const float mx = fmaxf(fmaxf(m0, m1), m_run[qt]);
-        // Only a masked subtile can leave a lane with no key seen so far.
-        mc = mx * c;
-        if (kUni || decltype(masked)::value) mc = (mx == -INFINITY) ? 0.0f : mc;
-        if (!decltype(exact)::value) mc_fix[qt] = mc;
-        l_run[qt] *= fast_exp2(m_run[qt] * c - mc);
-        m_run[qt] = mx;
-      } else {
-        mc = mc_fix[qt];
       }
-      float sp[4];
+    }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sp[r] = fast_exp2(fmaf(acc[r], c, -mc));
-#pragma unroll
-      for (int r = 4; r < 16; ++r) sp[r & 3] += fast_exp2(fmaf(acc[r], c, -mc));
-      l_run[qt] += (sp[0] + sp[1]) + (sp[2] + sp[3]);
+    for (int e = i * kElems / kRegions; e < (i + 1) * kElems / kRegions; ++e) {
+      const int qt = e / 16, r = e % 16;
+      const float x = fast_exp2(fmaf(accs[qt][r], c, -mcur[qt]));
+      if (r < 4) sp1[qt][r] = x;
+      else sp1[qt][r & 3] += x;
+      if (r == 15) l_run[qt] += (sp1[qt][0] + sp1[qt][1]) + (sp1[qt][2] + sp1[qt][3]);
     }
   };
   // Key tiles: all of the window, or (unidirectional) up to the tile holding
@@ -391,15 +444,23 @@ __global__ __launch_bounds__(ScoreCfg<T>::kThreads, ScoreCfg<T>::kMinWavesPerEU)
       l_run[qt] = 0.0f;
     }
     prologue(T1);
-    mma_sub(acc[0], 0, 0, std::true_type());
+    start_pass(std::true_type());
+    if constexpr (!decltype(exact)::value) {
+      // the reference: the maximum of the lane's first 16 keys
+      mask_sub(acc[0], 0, true);
+#pragma unroll
+      for (int qt = 0; qt < kRT; ++qt) {
+        m_run[qt] = lane_max(acc[0][qt]);
+        mc_fix[qt] = (m_run[qt] == -INFINITY) ? 0.0f : m_run[qt] * c;
+      }
+    }
     for (int t = 0; t + 1 < T1; ++t) {
       const int bt = t % 3, bn = (t + 1) % 3;
 #pragma unroll
       for (int k = 0; k < kSub; ++k) {
-        if (k + 1 < kSub) mma_sub(acc[(k + 1) & 1], bt, k + 1, std::true_type());
-        else mma_sub(acc[0], bn, 0, std::true_type());
-        stats_sub(acc[k & 1], t * kKeyTile + 32 * k, std::false_type(), exact, t == 0 && k == 0);
-        interleave();
+        step(acc[(k + 1) & 1], k + 1 < kSub ? bt : bn, (k + 1) % kSub, k + 2 < kSub ? bt : bn, (k + 2) % kSub,
+             true, true, std::true_type(),
+             [&](int i) { stats_valu(acc[k & 1], t * kKeyTile + 32 * k, false, exact, i); });
         pin();
       }
       store_tile(stage0, (t + 2) % 3);
@@ -410,16 +471,24 @@ __global__ __launch_bounds__(ScoreCfg<T>::kThreads, ScoreCfg<T>::kMinWavesPerEU)
       const int t = T1 - 1, bt = t % 3;
 #pragma unroll
       for (int k = 0; k < kSub; ++k) {
-        if (k + 1 < kSub) mma_sub(acc[(k + 1) & 1], bt, k + 1, std::true_type());
-        stats_sub(acc[k & 1], t * kKeyTile + 32 * k, std::true_type(), exact, t == 0 && k == 0);
+        step(acc[(k + 1) & 1], bt, (k + 1) % kSub, bt, (k + 2) % kSub, k + 1 < kSub, k + 2 < kSub,
+             std::true_type(), [&](int i) { stats_valu(acc[k & 1], t * kKeyTile + 32 * k, true, exact, i); });
       }
     }
   };
+  // The first two key tiles of pass 2 are fetched now, to arrive while
+  // pass 1 is checked and the row biases are published; they are stored once
+  // every wave is past pass 1 (its LDS tiles are then free).
+  Stage p2_t0, p2_t1;
   if constexpr (kUni) {
     pass1(std::true_type());
+    load_tile(p2_t0, 0);
+    load_tile(p2_t1, (T2 > 1 ? 1 : 0) * kKeyTile);
     __syncthreads();
   } else {
     pass1(std::false_type());
+    load_tile(p2_t0, 0);
+    load_tile(p2_t1, (T2 > 1 ? 1 : 0) * kKeyTile);
     bool bad = false;
 #pragma unroll
     for (int qt = 0; qt < kRT; ++qt) bad = bad || !(l_run[qt] < INFINITY) || m_run[qt] == -INFINITY;
@@ -444,7 +513,10 @@ __global__ __launch_bounds__(ScoreCfg<T>::kThreads, ScoreCfg<T>::kMinWavesPerEU)
     const float bias = (row < rows) ? mc + log2f(sum) : INFINITY;
     if (lane < 32) bias_lds[wave * kRowsPerWave + qt * 32 + lane] = bias;
   }
+  store_tile(p2_t0, 0);
+  store_tile(p2_t1, 1);
   __syncthreads();
+  load_tile(stage0, (T2 > 2 ? 2 : T2 - 1) * kKeyTile);
 
   // ---------------- pass 2: column sums over keys j < C ---------------------
   float nbias[kRT][16];
@@ -454,39 +526,34 @@ __global__ __launch_bounds__(ScoreCfg<T>::kThreads, ScoreCfg<T>::kMinWavesPerEU)
     for (int r = 0; r < 16; ++r)
       nbias[qt][r] = -bias_lds[wave * kRowsPerWave + qt * 32 + acc_row(r, lane)];
   float* out = a.out + ((size_t)unit * a.n_split + chunk) * C;
-  auto col_sub = [&](const Acc& accs, int t, int kt) {
-    float sp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    bool plain = true;
+  float sp2[4];
+  bool plain = true;
+  int lim2[kRT];
+  // VALU chunk i of pass 2 on slice kt of key tile t: each lane adds the
+  // probabilities of its key over its 16 rows of every query tile; the two
+  // lane halves (disjoint rows) go to LDS separately.
+  auto col_valu = [&](const Acc& accs, int t, int kt, int i) {
     if constexpr (kUni) {
-      const int key0 = t * kKeyTile + kt * 32;
-      if (key0 + 31 > i_wave) {
+      if (i == 0) {
+        const int key0 = t * kKeyTile + kt * 32;
         // row = row0 + qt*32 + acc_row(r, lane) sees key = key0 + lane%32
         // iff key*G <= row
-        plain = false;
+        plain = !(key0 + 31 > i_wave);
 #pragma unroll
-        for (int qt = 0; qt < kRT; ++qt) {
-          const int lim = (key0 + (lane & 31)) * G - row0 - qt * 32 - 4 * (lane >> 5);
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float e = fast_exp2(fmaf(accs[qt][r], c, nbias[qt][r]));
-            sp[r & 3] += (8 * (r >> 2) + (r & 3) >= lim) ? e : 0.0f;
-          }
-        }
+        for (int qt = 0; qt < kRT; ++qt)
+          lim2[qt] = (key0 + (lane & 31)) * G - row0 - qt * 32 - 4 * (lane >> 5);
       }
     }
-    if (plain) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sp[r] = fast_exp2(fmaf(accs[0][r], c, nbias[0][r]));
-#pragma unroll
-      for (int r = 4; r < 16; ++r) sp[r & 3] += fast_exp2(fmaf(accs[0][r], c, nbias[0][r]));
-#pragma unroll
-      for (int qt = 1; qt < kRT; ++qt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sp[r & 3] += fast_exp2(fmaf(accs[qt][r], c, nbias[qt][r]));
+    for (int e = i * kElems / kRegions; e < (i + 1) * kElems / kRegions; ++e) {
+      const int qt = e / 16, r = e % 16;
+      float x = fast_exp2(fmaf(accs[qt][r], c, nbias[qt][r]));
+      if constexpr (kUni) x = (plain || 8 * (r >> 2) + (r & 3) >= lim2[qt]) ? x : 0.0f;
+      if (e < 4) sp2[e] = x;
+      else sp2[e & 3] += x;
     }
-    float col = (sp[0] + sp[1]) + (sp[2] + sp[3]);
-    col += __shfl_xor(col, 32);
-    if (lane < 32) col_ring[t & 1][wave][kt * 32 + lane] = col;
+    if (i == kRegions - 1)
+      col_ring[t & 1][wave][lane >> 5][kt * 32 + (lane & 31)] = (sp2[0] + sp2[1]) + (sp2[2] + sp2[3]);
   };
   auto flush_cols = [&](int t) {
     // waves 0 .. kKeyTile/64 - 1 each add up 64 keys' per-wave partials
@@ -494,21 +561,20 @@ __global__ __launch_bounds__(ScoreCfg<T>::kThreads, ScoreCfg<T>::kMinWavesPerEU)
     if (wave < kKeyTile / 64 && key < C) {
       float sum = 0.0f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) sum += col_ring[t & 1][w][wave * 64 + lane];
+      for (int w = 0; w < kWaves; ++w)
+        sum += col_ring[t & 1][w][0][wave * 64 + lane] + col_ring[t & 1][w][1][wave * 64 + lane];
       out[key] = sum;
     }
   };
-  prologue(T2);
-  mma_sub(acc[0], 0, 0, std::false_type());
+  start_pass(std::false_type());
   for (int t = 0; t + 1 < T2; ++t) {
     const int bt = t % 3, bn = (t + 1) % 3;
     if (t > 0) flush_cols(t - 1);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int k = 0; k < kSub; ++k) {
-      if (k + 1 < kSub) mma_sub(acc[(k + 1) & 1], bt, k + 1, std::false_type());
-      else mma_sub(acc[0], bn, 0, std::false_type());
-      col_sub(acc[k & 1], t, k);
-      interleave();
+      step(acc[(k + 1) & 1], k + 1 < kSub ? bt : bn, (k + 1) % kSub, k + 2 < kSub ? bt : bn, (k + 2) % kSub, true,
+           true, std::false_type(), [&](int i) { col_valu(acc[k & 1], t, k, i); });
     }
     store_tile(stage0, (t + 2) % 3);
     __syncthreads();
@@ -517,10 +583,11 @@ __global__ __launch_bounds__(ScoreCfg<T>::kThreads, ScoreCfg<T>::kMinWavesPerEU)
   {
     const int t = T2 - 1, bt = t % 3;
     if (t > 0) flush_cols(t - 1);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int k = 0; k < kSub; ++k) {
-      if (k + 1 < kSub) mma_sub(acc[(k + 1) & 1], bt, k + 1, std::false_type());
-      col_sub(acc[k & 1], t, k);
+      step(acc[(k + 1) & 1], bt, (k + 1) % kSub, bt, (k + 2) % kSub, k + 1 < kSub, k + 2 < kSub, std::false_type(),
+           [&](int i) { col_valu(acc[k & 1], t, k, i); });
     }
     __syncthreads();
     flush_cols(t);
