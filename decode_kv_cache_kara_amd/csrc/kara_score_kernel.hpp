@@ -91,6 +91,10 @@ struct ScoreCfg {
   // Keys per LDS tile (one barrier each).  128-key tiles halve the barriers
   // and fit in LDS for bf16 but measured within 1 % of 64-key tiles.
   static constexpr int kKeyTile = 64;
+  // Consecutive 512-row chunks of one unit scored by one workgroup: the unit's
+  // K row offsets are staged once, and each next chunk's query fragments are
+  // loaded while the previous chunk finishes.
+  static constexpr int kChunksPerWG = sizeof(T) == 2 ? 2 : 1;
 };
 
 
@@ -139,6 +143,7 @@ __global__ __launch_bounds__(ScoreCfg<T>::kThreads, ScoreCfg<T>::kMinWavesPerEU)
   constexpr int kWaves = ScoreCfg<T>::kWaves;
   constexpr int kThreads = ScoreCfg<T>::kThreads;
   constexpr int kKeyTile = ScoreCfg<T>::kKeyTile;
+  constexpr int kChunksPerWG = ScoreCfg<T>::kChunksPerWG;
   constexpr int kSub = kKeyTile / 32;               // 32-key subtiles per tile
   using M = Mma<T>;
   typedef typename M::Frag Frag;
@@ -155,13 +160,15 @@ __global__ __launch_bounds__(ScoreCfg<T>::kThreads, ScoreCfg<T>::kMinWavesPerEU)
   __shared__ uint64_t s_off[kMaxWindow];           // byte offsets of the window's K rows
   __shared__ int s_redo;                            // pass 1 must run again exactly
 
-  // Block -> (unit, chunk).  Consecutive block ids go to different XCDs, so
-  // unit = slot-group * 8 + xcd keeps all chunks of a unit on one XCD.
+  // Block -> (unit, first chunk).  Consecutive block ids go to different
+  // XCDs, so unit = slot-group * 8 + xcd keeps all chunks of a unit on one
+  // XCD; a block scores kChunksPerWG consecutive chunks.
   const int bid = blockIdx.x;
   const int xcd = bid & 7;
   const int slot = bid >> 3;
-  const int unit = (slot / a.n_split) * 8 + xcd;
-  const int chunk = slot % a.n_split;
+  const int groups = (a.n_split + kChunksPerWG - 1) / kChunksPerWG;
+  const int unit = (slot / groups) * 8 + xcd;
+  int chunk = (slot % groups) * kChunksPerWG;
   if (unit >= a.n_units) return;  // uniform for the whole block
 
   const int h = unit % a.Hkv;
@@ -198,7 +205,7 @@ __global__ __launch_bounds__(ScoreCfg<T>::kThreads, ScoreCfg<T>::kMinWavesPerEU)
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int row0 = chunk * kScoreRowsPerChunk + wave * kRowsPerWave;
+  int row0 = chunk * kScoreRowsPerChunk + wave * kRowsPerWave;
 
   // Start-up order: the block table reads are issued first and the query
   // fragment loads after them, so the K row offsets (which need only the
@@ -213,23 +220,26 @@ __global__ __launch_bounds__(ScoreCfg<T>::kThreads, ScoreCfg<T>::kMinWavesPerEU)
     blk[u] = j < W ? trow[(start + j) >> a.bs_shift] : 0;
   }
 
-  // Query fragments of this wave's rows, kept in registers for both passes.
-  // Row r is window position r / G, head r % G of the group.
+  // Query fragments of this wave's rows (from row r0 on), kept in registers
+  // for both passes.  Row r is window position r / G, head r % G of the group.
   Frag qf[kRT][NK];
+  auto load_q = [&](int r0) {
 #pragma unroll
-  for (int qt = 0; qt < kRT; ++qt) {
-    const int row = row0 + qt * 32 + (lane & 31);
-    if (row < rows) {
-      const int i = row / G, g = row - (row / G) * G;
-      const int slot_i = i + ring_off < W ? i + ring_off : i + ring_off - W;
-      const T* p = qbase + ((size_t)slot_i * a.Hq + g) * D + (lane >> 5) * M::kPerLane;
+    for (int qt = 0; qt < kRT; ++qt) {
+      const int row = r0 + qt * 32 + (lane & 31);
+      if (row < rows) {
+        const int i = row / G, g = row - (row / G) * G;
+        const int slot_i = i + ring_off < W ? i + ring_off : i + ring_off - W;
+        const T* p = qbase + ((size_t)slot_i * a.Hq + g) * D + (lane >> 5) * M::kPerLane;
 #pragma unroll
-      for (int ks = 0; ks < NK; ++ks) qf[qt][ks] = *(const Frag*)(p + ks * M::kStep);
-    } else {
+        for (int ks = 0; ks < NK; ++ks) qf[qt][ks] = *(const Frag*)(p + ks * M::kStep);
+      } else {
 #pragma unroll
-      for (int ks = 0; ks < NK; ++ks) qf[qt][ks] = M::zero();
+        for (int ks = 0; ks < NK; ++ks) qf[qt][ks] = M::zero();
+      }
     }
-  }
+  };
+  load_q(row0);
 
   // Global -> register staging of key tiles: a tile is fetched one tile ahead
   // of its LDS store.  The byte offset of every window row's K row (its
@@ -350,251 +360,262 @@ __global__ __launch_bounds__(ScoreCfg<T>::kThreads, ScoreCfg<T>::kMinWavesPerEU)
     step(acc[0], 0, 0, 0, 1, true, true, keys_on_m, [](int) {});
   };
 
-  // ---------------- pass 1: row max and exp-sum over all W keys -------------
-  float m_run[kRT], l_run[kRT];
-  // Unidirectional: each lane's query positions, and the first position of
-  // the wave (subtiles whose last key is past it cross the diagonal).
-  int i_lane[kRT];
-#pragma unroll
-  for (int qt = 0; qt < kRT; ++qt) i_lane[qt] = (row0 + qt * 32 + (lane & 31)) / G;
-  const int i_wave = row0 / G;
-  // Keeps a step's VALU results ahead of the point that follows.
-  auto pin = [&]() {
-#pragma unroll
-    for (int qt = 0; qt < kRT; ++qt) asm volatile("" ::"v"(m_run[qt]), "v"(l_run[qt]));
-  };
-  // Two ways to accumulate the row statistics.  Exact: a running maximum,
-  // updated every subtile, with the sum rescaled when it moves.  Fixed
-  // reference (the method's scoring, not the unidirectional ablation): the
-  // maximum of the lane's first 16 keys is the reference for the whole row, so
-  // every subtile costs one multiply-add, one exp2 and one add per logit.  The
-  // sum is then exact in the same way (it is scaled by a power of two fixed
-  // per row) unless a later logit exceeds the reference by more than the
-  // float range allows (about 88 nats) or the lane saw no key in its first
-  // subtile; then the whole workgroup runs pass 1 again exactly.
-  float mc_fix[kRT], mcur[kRT], sp1[kRT][4];
-  auto mask_sub = [&](Acc& accs, int key0, bool tail) {
-#pragma unroll
-    for (int qt = 0; qt < kRT; ++qt) {
-      f32x16& v = accs[qt];
-      if constexpr (kUni) {
-        if (key0 + 31 > i_wave) {
-          // key = key0 + acc_row(r, lane) is seen iff key <= i_lane
-          const int lim = i_lane[qt] - key0 - 4 * (lane >> 5);
-#pragma unroll
+  // ---------------- the workgroup's chunks, one after another ---------------
+  for (int ci = 0;; ++ci) {
+    // another chunk follows: its query fragments are loaded during this
+    // chunk's last VALU-only step, once these are no longer read
+    const bool more = ci + 1 < kChunksPerWG && chunk + 1 < a.n_split;
+    // ---------------- pass 1: row max and exp-sum over all W keys -------------
+    float m_run[kRT], l_run[kRT];
+    // Unidirectional: each lane's query positions, and the first position of
+    // the wave (subtiles whose last key is past it cross the diagonal).
+    int i_lane[kRT];
+  #pragma unroll
+    for (int qt = 0; qt < kRT; ++qt) i_lane[qt] = (row0 + qt * 32 + (lane & 31)) / G;
+    const int i_wave = row0 / G;
+    // Keeps a step's VALU results ahead of the point that follows.
+    auto pin = [&]() {
+  #pragma unroll
+      for (int qt = 0; qt < kRT; ++qt) asm volatile("" ::"v"(m_run[qt]), "v"(l_run[qt]));
+    };
+    // Two ways to accumulate the row statistics.  Exact: a running maximum,
+    // updated every subtile, with the sum rescaled when it moves.  Fixed
+    // reference (the method's scoring, not the unidirectional ablation): the
+    // maximum of the lane's first 16 keys is the reference for the whole row, so
+    // every subtile costs one multiply-add, one exp2 and one add per logit.  The
+    // sum is then exact in the same way (it is scaled by a power of two fixed
+    // per row) unless a later logit exceeds the reference by more than the
+    // float range allows (about 88 nats) or the lane saw no key in its first
+    // subtile; then the whole workgroup runs pass 1 again exactly.
+    float mc_fix[kRT], mcur[kRT], sp1[kRT][4];
+    auto mask_sub = [&](Acc& accs, int key0, bool tail) {
+  #pragma unroll
+      for (int qt = 0; qt < kRT; ++qt) {
+        f32x16& v = accs[qt];
+        if constexpr (kUni) {
+          if (key0 + 31 > i_wave) {
+            // key = key0 + acc_row(r, lane) is seen iff key <= i_lane
+            const int lim = i_lane[qt] - key0 - 4 * (lane >> 5);
+  #pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (8 * (r >> 2) + (r & 3) > lim) v[r] = -INFINITY;
+          }
+        } else if (tail) {
+  #pragma unroll
           for (int r = 0; r < 16; ++r)
-            if (8 * (r >> 2) + (r & 3) > lim) v[r] = -INFINITY;
+            if (key0 + acc_row(r, lane) >= W) v[r] = -INFINITY;
         }
-      } else if (tail) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (key0 + acc_row(r, lane) >= W) v[r] = -INFINITY;
       }
+    };
+    auto lane_max = [&](const f32x16& v) {
+      float m0 = fmaxf(v[0], v[1]), m1 = fmaxf(v[8], v[9]);
+  #pragma unroll
+      for (int r = 2; r < 8; ++r) {
+        m0 = fmaxf(m0, v[r]);
+        m1 = fmaxf(m1, v[8 + r]);
+      }
+      return fmaxf(m0, m1);
+    };
+    // VALU chunk i of pass 1 on the subtile starting at key0.
+    auto stats_valu = [&](Acc& accs, int key0, bool tail, auto exact, int i) {
+      if (i == 0) {
+        mask_sub(accs, key0, tail);
+  #pragma unroll
+        for (int qt = 0; qt < kRT; ++qt) {
+          if constexpr (decltype(exact)::value) {
+            const float mx = fmaxf(lane_max(accs[qt]), m_run[qt]);
+            const float mc = (mx == -INFINITY) ? 0.0f : mx * c;
+            l_run[qt] *= fast_exp2(m_run[qt] * c - mc);
+            m_run[qt] = mx;
+            mcur[qt] = mc;
+          } else {
+            mcur[qt] = mc_fix[qt];
+          }
+        }
+      }
+  #pragma unroll
+      for (int e = i * kElems / kRegions; e < (i + 1) * kElems / kRegions; ++e) {
+        const int qt = e / 16, r = e % 16;
+        const float x = fast_exp2(fmaf(accs[qt][r], c, -mcur[qt]));
+        if (r < 4) sp1[qt][r] = x;
+        else sp1[qt][r & 3] += x;
+        if (r == 15) l_run[qt] += (sp1[qt][0] + sp1[qt][1]) + (sp1[qt][2] + sp1[qt][3]);
+      }
+    };
+    // Key tiles: all of the window, or (unidirectional) up to the tile holding
+    // the position of the workgroup's last row.  Uniform over the workgroup.
+    int T1 = (W + kKeyTile - 1) / kKeyTile;
+    int T2 = (C + kKeyTile - 1) / kKeyTile;
+    if constexpr (kUni) {
+      const int last_row = min(rows, (chunk + 1) * kScoreRowsPerChunk) - 1;
+      const int i_last = last_row / G;
+      T1 = i_last / kKeyTile + 1;
+      T2 = min(C - 1, i_last) / kKeyTile + 1;
     }
-  };
-  auto lane_max = [&](const f32x16& v) {
-    float m0 = fmaxf(v[0], v[1]), m1 = fmaxf(v[8], v[9]);
-#pragma unroll
-    for (int r = 2; r < 8; ++r) {
-      m0 = fmaxf(m0, v[r]);
-      m1 = fmaxf(m1, v[8 + r]);
-    }
-    return fmaxf(m0, m1);
-  };
-  // VALU chunk i of pass 1 on the subtile starting at key0.
-  auto stats_valu = [&](Acc& accs, int key0, bool tail, auto exact, int i) {
-    if (i == 0) {
-      mask_sub(accs, key0, tail);
-#pragma unroll
+    auto pass1 = [&](auto exact) {
+  #pragma unroll
       for (int qt = 0; qt < kRT; ++qt) {
-        if constexpr (decltype(exact)::value) {
-          const float mx = fmaxf(lane_max(accs[qt]), m_run[qt]);
-          const float mc = (mx == -INFINITY) ? 0.0f : mx * c;
-          l_run[qt] *= fast_exp2(m_run[qt] * c - mc);
-          m_run[qt] = mx;
-          mcur[qt] = mc;
-        } else {
-          mcur[qt] = mc_fix[qt];
+        m_run[qt] = -INFINITY;
+        l_run[qt] = 0.0f;
+      }
+      prologue(T1);
+      start_pass(std::true_type());
+      if constexpr (!decltype(exact)::value) {
+        // the reference: the maximum of the lane's first 16 keys
+        mask_sub(acc[0], 0, true);
+  #pragma unroll
+        for (int qt = 0; qt < kRT; ++qt) {
+          m_run[qt] = lane_max(acc[0][qt]);
+          mc_fix[qt] = (m_run[qt] == -INFINITY) ? 0.0f : m_run[qt] * c;
         }
       }
+      for (int t = 0; t + 1 < T1; ++t) {
+        const int bt = t % 3, bn = (t + 1) % 3;
+  #pragma unroll
+        for (int k = 0; k < kSub; ++k) {
+          step(acc[(k + 1) & 1], k + 1 < kSub ? bt : bn, (k + 1) % kSub, k + 2 < kSub ? bt : bn, (k + 2) % kSub,
+               true, true, std::true_type(),
+               [&](int i) { stats_valu(acc[k & 1], t * kKeyTile + 32 * k, false, exact, i); });
+          pin();
+        }
+        store_tile(stage0, (t + 2) % 3);
+        __syncthreads();
+        load_tile(stage0, (t + 3 < T1 ? t + 3 : T1 - 1) * kKeyTile);
+      }
+      {
+        const int t = T1 - 1, bt = t % 3;
+  #pragma unroll
+        for (int k = 0; k < kSub; ++k) {
+          step(acc[(k + 1) & 1], bt, (k + 1) % kSub, bt, (k + 2) % kSub, k + 1 < kSub, k + 2 < kSub,
+               std::true_type(), [&](int i) { stats_valu(acc[k & 1], t * kKeyTile + 32 * k, true, exact, i); });
+        }
+      }
+    };
+    // The first two key tiles of pass 2 are fetched now, to arrive while
+    // pass 1 is checked and the row biases are published; they are stored once
+    // every wave is past pass 1 (its LDS tiles are then free).
+    Stage p2_t0, p2_t1;
+    if constexpr (kUni) {
+      pass1(std::true_type());
+      load_tile(p2_t0, 0);
+      load_tile(p2_t1, (T2 > 1 ? 1 : 0) * kKeyTile);
+      __syncthreads();
+    } else {
+      pass1(std::false_type());
+      load_tile(p2_t0, 0);
+      load_tile(p2_t1, (T2 > 1 ? 1 : 0) * kKeyTile);
+      bool bad = false;
+  #pragma unroll
+      for (int qt = 0; qt < kRT; ++qt) bad = bad || !(l_run[qt] < INFINITY) || m_run[qt] == -INFINITY;
+      if (__ballot(bad) && lane == 0) s_redo = 1;
+      __syncthreads();
+      if (s_redo) {                                   // uniform over the workgroup
+        pass1(std::true_type());
+        __syncthreads();
+      }
     }
-#pragma unroll
-    for (int e = i * kElems / kRegions; e < (i + 1) * kElems / kRegions; ++e) {
-      const int qt = e / 16, r = e % 16;
-      const float x = fast_exp2(fmaf(accs[qt][r], c, -mcur[qt]));
-      if (r < 4) sp1[qt][r] = x;
-      else sp1[qt][r & 3] += x;
-      if (r == 15) l_run[qt] += (sp1[qt][0] + sp1[qt][1]) + (sp1[qt][2] + sp1[qt][3]);
-    }
-  };
-  // Key tiles: all of the window, or (unidirectional) up to the tile holding
-  // the position of the workgroup's last row.  Uniform over the workgroup.
-  int T1 = (W + kKeyTile - 1) / kKeyTile;
-  int T2 = (C + kKeyTile - 1) / kKeyTile;
-  if constexpr (kUni) {
-    const int last_row = min(rows, (chunk + 1) * kScoreRowsPerChunk) - 1;
-    const int i_last = last_row / G;
-    T1 = i_last / kKeyTile + 1;
-    T2 = min(C - 1, i_last) / kKeyTile + 1;
-  }
-  auto pass1 = [&](auto exact) {
-#pragma unroll
+
+    // Merge the two lane halves (same query, disjoint keys) and publish the row
+    // bias  m*c + log2(sum)  so that  p = exp2(x*c - bias).
+  #pragma unroll
     for (int qt = 0; qt < kRT; ++qt) {
-      m_run[qt] = -INFINITY;
-      l_run[qt] = 0.0f;
+      const float mo = __shfl_xor(m_run[qt], 32);
+      const float lo = __shfl_xor(l_run[qt], 32);
+      const float mm = fmaxf(m_run[qt], mo);
+      const float mc = mm * c;
+      const float sum = l_run[qt] * fast_exp2(m_run[qt] * c - mc) + lo * fast_exp2(mo * c - mc);
+      const int row = row0 + qt * 32 + (lane & 31);
+      const float bias = (row < rows) ? mc + log2f(sum) : INFINITY;
+      if (lane < 32) bias_lds[wave * kRowsPerWave + qt * 32 + lane] = bias;
     }
-    prologue(T1);
-    start_pass(std::true_type());
-    if constexpr (!decltype(exact)::value) {
-      // the reference: the maximum of the lane's first 16 keys
-      mask_sub(acc[0], 0, true);
-#pragma unroll
-      for (int qt = 0; qt < kRT; ++qt) {
-        m_run[qt] = lane_max(acc[0][qt]);
-        mc_fix[qt] = (m_run[qt] == -INFINITY) ? 0.0f : m_run[qt] * c;
+    store_tile(p2_t0, 0);
+    store_tile(p2_t1, 1);
+    __syncthreads();
+    if (tid == 0) s_redo = 0;                       // every wave has read it
+    load_tile(stage0, (T2 > 2 ? 2 : T2 - 1) * kKeyTile);
+
+    // ---------------- pass 2: column sums over keys j < C ---------------------
+    float nbias[kRT][16];
+  #pragma unroll
+    for (int qt = 0; qt < kRT; ++qt)
+  #pragma unroll
+      for (int r = 0; r < 16; ++r)
+        nbias[qt][r] = -bias_lds[wave * kRowsPerWave + qt * 32 + acc_row(r, lane)];
+    float* out = a.out + ((size_t)unit * a.n_split + chunk) * C;
+    float sp2[4];
+    bool plain = true;
+    int lim2[kRT];
+    // VALU chunk i of pass 2 on slice kt of key tile t: each lane adds the
+    // probabilities of its key over its 16 rows of every query tile; the two
+    // lane halves (disjoint rows) go to LDS separately.
+    auto col_valu = [&](const Acc& accs, int t, int kt, int i) {
+      if constexpr (kUni) {
+        if (i == 0) {
+          const int key0 = t * kKeyTile + kt * 32;
+          // row = row0 + qt*32 + acc_row(r, lane) sees key = key0 + lane%32
+          // iff key*G <= row
+          plain = !(key0 + 31 > i_wave);
+  #pragma unroll
+          for (int qt = 0; qt < kRT; ++qt)
+            lim2[qt] = (key0 + (lane & 31)) * G - row0 - qt * 32 - 4 * (lane >> 5);
+        }
       }
-    }
-    for (int t = 0; t + 1 < T1; ++t) {
+  #pragma unroll
+      for (int e = i * kElems / kRegions; e < (i + 1) * kElems / kRegions; ++e) {
+        const int qt = e / 16, r = e % 16;
+        float x = fast_exp2(fmaf(accs[qt][r], c, nbias[qt][r]));
+        if constexpr (kUni) x = (plain || 8 * (r >> 2) + (r & 3) >= lim2[qt]) ? x : 0.0f;
+        if (e < 4) sp2[e] = x;
+        else sp2[e & 3] += x;
+      }
+      if (i == kRegions - 1)
+        col_ring[t & 1][wave][lane >> 5][kt * 32 + (lane & 31)] = (sp2[0] + sp2[1]) + (sp2[2] + sp2[3]);
+    };
+    auto flush_cols = [&](int t) {
+      // waves 0 .. kKeyTile/64 - 1 each add up 64 keys' per-wave partials
+      const int key = t * kKeyTile + wave * 64 + lane;
+      if (wave < kKeyTile / 64 && key < C) {
+        float sum = 0.0f;
+  #pragma unroll
+        for (int w = 0; w < kWaves; ++w)
+          sum += col_ring[t & 1][w][0][wave * 64 + lane] + col_ring[t & 1][w][1][wave * 64 + lane];
+        out[key] = sum;
+      }
+    };
+    start_pass(std::false_type());
+    for (int t = 0; t + 1 < T2; ++t) {
       const int bt = t % 3, bn = (t + 1) % 3;
-#pragma unroll
+      if (t > 0) flush_cols(t - 1);
+      __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
       for (int k = 0; k < kSub; ++k) {
-        step(acc[(k + 1) & 1], k + 1 < kSub ? bt : bn, (k + 1) % kSub, k + 2 < kSub ? bt : bn, (k + 2) % kSub,
-             true, true, std::true_type(),
-             [&](int i) { stats_valu(acc[k & 1], t * kKeyTile + 32 * k, false, exact, i); });
-        pin();
+        step(acc[(k + 1) & 1], k + 1 < kSub ? bt : bn, (k + 1) % kSub, k + 2 < kSub ? bt : bn, (k + 2) % kSub, true,
+             true, std::false_type(), [&](int i) { col_valu(acc[k & 1], t, k, i); });
       }
       store_tile(stage0, (t + 2) % 3);
       __syncthreads();
-      load_tile(stage0, (t + 3 < T1 ? t + 3 : T1 - 1) * kKeyTile);
+      load_tile(stage0, (t + 3 < T2 ? t + 3 : T2 - 1) * kKeyTile);
     }
     {
-      const int t = T1 - 1, bt = t % 3;
-#pragma unroll
+      const int t = T2 - 1, bt = t % 3;
+      if (t > 0) flush_cols(t - 1);
+      __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
       for (int k = 0; k < kSub; ++k) {
-        step(acc[(k + 1) & 1], bt, (k + 1) % kSub, bt, (k + 2) % kSub, k + 1 < kSub, k + 2 < kSub,
-             std::true_type(), [&](int i) { stats_valu(acc[k & 1], t * kKeyTile + 32 * k, true, exact, i); });
+        if (k == kSub - 1 && more) load_q(row0 + kScoreRowsPerChunk);
+        step(acc[(k + 1) & 1], bt, (k + 1) % kSub, bt, (k + 2) % kSub, k + 1 < kSub, k + 2 < kSub, std::false_type(),
+             [&](int i) { col_valu(acc[k & 1], t, k, i); });
       }
-    }
-  };
-  // The first two key tiles of pass 2 are fetched now, to arrive while
-  // pass 1 is checked and the row biases are published; they are stored once
-  // every wave is past pass 1 (its LDS tiles are then free).
-  Stage p2_t0, p2_t1;
-  if constexpr (kUni) {
-    pass1(std::true_type());
-    load_tile(p2_t0, 0);
-    load_tile(p2_t1, (T2 > 1 ? 1 : 0) * kKeyTile);
-    __syncthreads();
-  } else {
-    pass1(std::false_type());
-    load_tile(p2_t0, 0);
-    load_tile(p2_t1, (T2 > 1 ? 1 : 0) * kKeyTile);
-    bool bad = false;
-#pragma unroll
-    for (int qt = 0; qt < kRT; ++qt) bad = bad || !(l_run[qt] < INFINITY) || m_run[qt] == -INFINITY;
-    if (__ballot(bad) && lane == 0) s_redo = 1;
-    __syncthreads();
-    if (s_redo) {                                   // uniform over the workgroup
-      pass1(std::true_type());
       __syncthreads();
+      flush_cols(t);
     }
-  }
-
-  // Merge the two lane halves (same query, disjoint keys) and publish the row
-  // bias  m*c + log2(sum)  so that  p = exp2(x*c - bias).
-#pragma unroll
-  for (int qt = 0; qt < kRT; ++qt) {
-    const float mo = __shfl_xor(m_run[qt], 32);
-    const float lo = __shfl_xor(l_run[qt], 32);
-    const float mm = fmaxf(m_run[qt], mo);
-    const float mc = mm * c;
-    const float sum = l_run[qt] * fast_exp2(m_run[qt] * c - mc) + lo * fast_exp2(mo * c - mc);
-    const int row = row0 + qt * 32 + (lane & 31);
-    const float bias = (row < rows) ? mc + log2f(sum) : INFINITY;
-    if (lane < 32) bias_lds[wave * kRowsPerWave + qt * 32 + lane] = bias;
-  }
-  store_tile(p2_t0, 0);
-  store_tile(p2_t1, 1);
-  __syncthreads();
-  load_tile(stage0, (T2 > 2 ? 2 : T2 - 1) * kKeyTile);
-
-  // ---------------- pass 2: column sums over keys j < C ---------------------
-  float nbias[kRT][16];
-#pragma unroll
-  for (int qt = 0; qt < kRT; ++qt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      nbias[qt][r] = -bias_lds[wave * kRowsPerWave + qt * 32 + acc_row(r, lane)];
-  float* out = a.out + ((size_t)unit * a.n_split + chunk) * C;
-  float sp2[4];
-  bool plain = true;
-  int lim2[kRT];
-  // VALU chunk i of pass 2 on slice kt of key tile t: each lane adds the
-  // probabilities of its key over its 16 rows of every query tile; the two
-  // lane halves (disjoint rows) go to LDS separately.
-  auto col_valu = [&](const Acc& accs, int t, int kt, int i) {
     if constexpr (kUni) {
-      if (i == 0) {
-        const int key0 = t * kKeyTile + kt * 32;
-        // row = row0 + qt*32 + acc_row(r, lane) sees key = key0 + lane%32
-        // iff key*G <= row
-        plain = !(key0 + 31 > i_wave);
-#pragma unroll
-        for (int qt = 0; qt < kRT; ++qt)
-          lim2[qt] = (key0 + (lane & 31)) * G - row0 - qt * 32 - 4 * (lane >> 5);
-      }
+      // keys past the last tile get nothing from this chunk's rows
+      for (int key = T2 * kKeyTile + tid; key < C; key += kThreads) out[key] = 0.0f;
     }
-#pragma unroll
-    for (int e = i * kElems / kRegions; e < (i + 1) * kElems / kRegions; ++e) {
-      const int qt = e / 16, r = e % 16;
-      float x = fast_exp2(fmaf(accs[qt][r], c, nbias[qt][r]));
-      if constexpr (kUni) x = (plain || 8 * (r >> 2) + (r & 3) >= lim2[qt]) ? x : 0.0f;
-      if (e < 4) sp2[e] = x;
-      else sp2[e & 3] += x;
-    }
-    if (i == kRegions - 1)
-      col_ring[t & 1][wave][lane >> 5][kt * 32 + (lane & 31)] = (sp2[0] + sp2[1]) + (sp2[2] + sp2[3]);
-  };
-  auto flush_cols = [&](int t) {
-    // waves 0 .. kKeyTile/64 - 1 each add up 64 keys' per-wave partials
-    const int key = t * kKeyTile + wave * 64 + lane;
-    if (wave < kKeyTile / 64 && key < C) {
-      float sum = 0.0f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w)
-        sum += col_ring[t & 1][w][0][wave * 64 + lane] + col_ring[t & 1][w][1][wave * 64 + lane];
-      out[key] = sum;
-    }
-  };
-  start_pass(std::false_type());
-  for (int t = 0; t + 1 < T2; ++t) {
-    const int bt = t % 3, bn = (t + 1) % 3;
-    if (t > 0) flush_cols(t - 1);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int k = 0; k < kSub; ++k) {
-      step(acc[(k + 1) & 1], k + 1 < kSub ? bt : bn, (k + 1) % kSub, k + 2 < kSub ? bt : bn, (k + 2) % kSub, true,
-           true, std::false_type(), [&](int i) { col_valu(acc[k & 1], t, k, i); });
-    }
-    store_tile(stage0, (t + 2) % 3);
-    __syncthreads();
-    load_tile(stage0, (t + 3 < T2 ? t + 3 : T2 - 1) * kKeyTile);
-  }
-  {
-    const int t = T2 - 1, bt = t % 3;
-    if (t > 0) flush_cols(t - 1);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int k = 0; k < kSub; ++k) {
-      step(acc[(k + 1) & 1], bt, (k + 1) % kSub, bt, (k + 2) % kSub, k + 1 < kSub, k + 2 < kSub, std::false_type(),
-           [&](int i) { col_valu(acc[k & 1], t, k, i); });
-    }
-    __syncthreads();
-    flush_cols(t);
-  }
-  if constexpr (kUni) {
-    // keys past the last tile get nothing from this chunk's rows
-    for (int key = T2 * kKeyTile + tid; key < C; key += kThreads) out[key] = 0.0f;
+    if (!more) break;
+    ++chunk;
+    row0 += kScoreRowsPerChunk;
   }
 }
 
@@ -603,7 +624,8 @@ __global__ __launch_bounds__(ScoreCfg<T>::kThreads, ScoreCfg<T>::kMinWavesPerEU)
 template <typename T, int D>
 hipError_t launch_score_typed(const ScoreArgs& a, hipStream_t stream) {
   const int units_pad = (a.n_units + 7) / 8 * 8;
-  const unsigned grid = (unsigned)units_pad * (unsigned)a.n_split;
+  const unsigned groups = (unsigned)((a.n_split + ScoreCfg<T>::kChunksPerWG - 1) / ScoreCfg<T>::kChunksPerWG);
+  const unsigned grid = (unsigned)units_pad * groups;
   if (a.unidirectional)
     hipLaunchKernelGGL((score_kernel<T, D, true>), dim3(grid), dim3(ScoreCfg<T>::kThreads), 0, stream, a);
   else
