@@ -86,6 +86,60 @@ def cpu_baseline(cfg, n_layers_sample, seed, n_seqs_sample=3, flags=0):
                        f"shapes (L={[int(x) for x in lens]}), {dt:.1f} s, scaled to the full layer count")}
 
 
+def measured_ceilings(score_ms, exec_flop, exec_logits, compact_ms, compact_bytes):
+    """The chip's own ceilings for the scoring kernel's and the compaction's
+    kinds of work, from the library's probes (MFMA loop, per-logit VALU loop,
+    the two interleaved as in the scoring kernel's inner loop, streaming copy),
+    each timed with HIP events on its launch stream after one warm-up launch,
+    and the times those rates give for this launch's executed work."""
+    import torch
+
+    from decode_kv_cache_kara_amd import kara
+
+    stream = torch.cuda.current_stream()
+    scratch = torch.empty(kara.kara_probe_scratch_bytes() // 4, dtype=torch.float32, device="cuda")
+    n = 4 << 30
+    src = torch.ones(n // 4, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+
+    def rate(kind, iters, launches):
+        kw = {"src": src} if kind == kara.KARA_PROBE_COPY else {}
+        out_t = dst if kind == kara.KARA_PROBE_COPY else scratch
+        kara.kara_probe(kind, iters, out_t, stream=stream, **kw)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        work = sum(kara.kara_probe(kind, iters, out_t, stream=stream, **kw) for _ in range(launches))
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return work / (e0.elapsed_time(e1) / 1e3)
+
+    mfma = rate(kara.KARA_PROBE_MFMA, 100000, 3)          # flop/s
+    valu = rate(kara.KARA_PROBE_VALU, 50000, 3)           # elements/s
+    mix = rate(kara.KARA_PROBE_MIX, 10000, 3)             # logits/s
+    copy = rate(kara.KARA_PROBE_COPY, 1, 3)               # bytes/s
+    del src, dst, scratch
+    bound_ms = exec_logits / mix * 1e3
+    return {
+        "mfma_bf16_tflops": round(mfma / 1e12, 1),
+        "valu_softmax_gelem_per_s": round(valu / 1e9, 1),
+        "mix_glogits_per_s": round(mix / 1e9, 1),
+        "copy_gbs": round(copy / 1e9, 1),
+        "score_kernel": {
+            "executed_logits_per_launch": exec_logits,
+            "mfma_alone_ms": round(exec_flop / mfma * 1e3, 3),
+            "valu_alone_ms": round(exec_logits / valu * 1e3, 3),
+            "interleaved_ms": round(bound_ms, 3),
+            "measured_ms": round(score_ms, 3),
+            "frac_of_interleaved": round(bound_ms / score_ms, 4),
+        },
+        "compact_kernel": {"copy_ms": round(compact_bytes / copy * 1e3, 3), "measured_ms": round(compact_ms, 3),
+                           "frac_of_copy": round(compact_bytes / copy / (compact_ms / 1e3), 4)},
+        "note": ("probes of this library (include/kara.h, kara_probe) run on the same GPU after the timed steps; "
+                 "interleaved = the scoring kernel's inner loop (2*D MFMA flops and one multiply-add, exp2 and "
+                 "add per logit) without memory traffic"),
+    }
+
+
 def decode_attention_roofline(ses, wl, launches=36):
     """Decode attention over the cache as the last compression step left it
     (new tables and lengths): HBM bytes per launch = K and V rows of every
@@ -364,6 +418,13 @@ def main():
     out["decode_attention"] = decode_attention_roofline(ses, wl)
     log(f"decode attention over the compacted cache: {out['decode_attention']['ms_per_launch']:.3f} ms/layer, "
         f"{out['decode_attention']['achieved']:.0f} GB/s")
+    if wl.dtype == torch.bfloat16 and not uni:
+        exec_logits = exec_flop / (2.0 * D)
+        out["measured_ceilings"] = measured_ceilings(stage[0], exec_flop, exec_logits, stage[2], compact_bytes)
+        mc = out["measured_ceilings"]
+        log(f"measured ceilings: MFMA {mc['mfma_bf16_tflops']} TFLOP/s, softmax VALU {mc['valu_softmax_gelem_per_s']} "
+            f"Gelem/s, interleaved {mc['mix_glogits_per_s']} Glogit/s, copy {mc['copy_gbs']} GB/s; score kernel at "
+            f"{mc['score_kernel']['frac_of_interleaved']:.1%} of its interleaved bound")
     if args.flags == 0 and args.config == 2:       # costs scaled from the Qwen3-4B-shaped slice
         out["policy_sim"] = policy_sim(out, wl)
     if not args.no_cpu_baseline:

@@ -679,4 +679,37 @@ kara_status kara_schedule_step(int64_t step, int32_t period, int32_t window, int
   return KARA_OK;
 }
 
+static int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return n;
+}
+
+size_t kara_probe_scratch_bytes(void) {
+  const int n_cu = device_cus();
+  return n_cu > 0 ? (size_t)kara::probe_grid(n_cu) * 256 * sizeof(float) : 0;
+}
+
+kara_status kara_probe(int32_t kind, int64_t iters, void* dst_d, const void* src_d, size_t n_bytes, void* stream,
+                       double* work_out) {
+  if (!work_out) return fail(KARA_E_INVAL, "work_out is NULL");
+  if (kind < KARA_PROBE_MFMA || kind > KARA_PROBE_MIX) return fail(KARA_E_INVAL, "probe kind %d unknown", kind);
+  const int n_cu = device_cus();
+  if (n_cu < 1) return fail(KARA_E_HIP, "no current HIP device");
+  if (!dst_d) return fail(KARA_E_INVAL, "dst is NULL");
+  if (kind == KARA_PROBE_COPY) {
+    if (!src_d) return fail(KARA_E_INVAL, "src is NULL");
+    if (n_bytes % 16 != 0 || !is_aligned(dst_d, 16) || !is_aligned(src_d, 16))
+      return fail(KARA_E_INVAL, "copy probe: size and both addresses must be multiples of 16");
+  } else {
+    if (iters < 1) return fail(KARA_E_INVAL, "iters must be >= 1");
+    if (n_bytes < (size_t)kara::probe_grid(n_cu) * 256 * sizeof(float))
+      return fail(KARA_E_INVAL, "dst holds %zu bytes, the probe writes %zu", n_bytes,
+                  (size_t)kara::probe_grid(n_cu) * 256 * sizeof(float));
+  }
+  hipError_t e = kara::launch_probe(kind, iters, dst_d, src_d, n_bytes, n_cu, (hipStream_t)stream, work_out);
+  return e == hipSuccess ? KARA_OK : hip_fail(e, "probe launch");
+}
+
 }  // extern "C"

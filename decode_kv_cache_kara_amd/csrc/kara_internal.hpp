@@ -102,4 +102,11 @@ struct CompactArgs {
 
 hipError_t launch_compact(const CompactArgs& a, hipStream_t stream);
 
+// Measurement probes (kara_probe.hip): workgroups per launch of kinds 0, 1, 3
+// on a device with n_cu compute units, and the launch; *work receives the
+// launch's work in the kind's unit (flops, elements, bytes, logits).
+int probe_grid(int n_cu);
+hipError_t launch_probe(int kind, int64_t iters, void* dst, const void* src, size_t n_bytes, int n_cu,
+                        hipStream_t stream, double* work);
+
 }  // namespace kara

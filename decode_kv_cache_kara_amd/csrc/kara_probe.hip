@@ -1,0 +1,160 @@
+// Measured ceilings of this chip for the kinds of work the compression step
+// does, so that each kernel's rate can be set against what the part reaches
+// under the same kind of load (the nominal peaks assume the 2.4 GHz clock,
+// which a fully loaded MI355X does not hold):
+//   kind 0  matrix cores only: four independent chains of 32x32x16 bf16 MFMAs
+//           per wave, operands in registers;
+//   kind 1  the scoring kernel's per-logit VALU work alone: one multiply-add,
+//           one exp2 and one add per element, 16 independent elements per lane;
+//   kind 2  a streaming copy with 16-byte nontemporal loads and stores, eight
+//           loads in flight per lane;
+//   kind 3  kinds 0 and 1 interleaved in one wave exactly as the scoring kernel
+//           interleaves them: while the VALU turns one 64x32 logit tile into
+//           exponentials and sums, the matrix cores compute the next tile
+//           (2 * 128 MFMA flops per logit), in eight fenced regions of two
+//           MFMAs and four logits each.
+// Kinds 0, 1 and 3 run two waves per SIMD, the scoring kernel's occupancy.
+// This is a measurement aid of the benchmark, not part of the compression step.
+
+#include "kara_internal.hpp"
+
+namespace kara {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kProbeThreads = 256;
+
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Small operand values that depend on the lane (so nothing is constant).
+__device__ __forceinline__ bf16x8 operand(int lane, int salt) {
+  bf16x8 v;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = (__bf16)(0.0009765625f * (float)((lane * 7 + i * 3 + salt) % 13 - 6));
+  return v;
+}
+
+__global__ __launch_bounds__(kProbeThreads, 2) void probe_mfma(float* dst, int64_t iters) {
+  const int lane = threadIdx.x & 63;
+  const bf16x8 a0 = operand(lane, 0), a1 = operand(lane, 1), b0 = operand(lane, 2), b1 = operand(lane, 3);
+  f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  for (int64_t it = 0; it < iters; ++it) {
+    c0 = mfma(a0, b0, c0);
+    c1 = mfma(a1, b0, c1);
+    c2 = mfma(a0, b1, c2);
+    c3 = mfma(a1, b1, c3);
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s += (c0[r] + c1[r]) + (c2[r] + c3[r]);
+  dst[(size_t)blockIdx.x * kProbeThreads + threadIdx.x] = s;
+}
+
+__global__ __launch_bounds__(kProbeThreads, 2) void probe_valu(float* dst, int64_t iters, float c, float nb) {
+  float x[16], s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int k = 0; k < 16; ++k) x[k] = 0.01f * (float)((threadIdx.x + 5 * k) % 17);
+  for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const float e = __builtin_amdgcn_exp2f(fmaf(x[k], c, nb));
+      s[k & 3] += e;
+      x[k] = e;
+    }
+  }
+  dst[(size_t)blockIdx.x * kProbeThreads + threadIdx.x] = (s[0] + s[1]) + (s[2] + s[3]);
+}
+
+__global__ __launch_bounds__(kProbeThreads, 2) void probe_mix(float* dst, int64_t iters, float c, float nb) {
+  const int lane = threadIdx.x & 63;
+  bf16x8 q0[8], q1[8], kf[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    q0[i] = operand(lane, i);
+    q1[i] = operand(lane, 8 + i);
+    kf[i] = operand(lane, 16 + i);
+  }
+  f32x16 a0 = {}, a1 = {}, b0 = {}, b1 = {};
+  float sp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  // MFMAs into (n0, n1) while the VALU consumes (v0, v1); the accumulators are
+  // carried across iterations so that no MFMA is loop-invariant.
+  auto half = [&](f32x16& n0, f32x16& n1, const f32x16& v0, const f32x16& v1) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      n0 = mfma(q0[i], kf[i], n0);
+      n1 = mfma(q1[i], kf[i], n1);
+#pragma unroll
+      for (int e = 4 * i; e < 4 * i + 4; ++e) {
+        const float x = e < 16 ? v0[e] : v1[e - 16];
+        sp[e & 3] += __builtin_amdgcn_exp2f(fmaf(x, c, nb));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  for (int64_t it = 0; it < iters; ++it) {
+    half(a0, a1, b0, b1);
+    half(b0, b1, a0, a1);
+  }
+  float s = (sp[0] + sp[1]) + (sp[2] + sp[3]);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s += 1e-30f * ((a0[r] + a1[r]) + (b0[r] + b1[r]));
+  dst[(size_t)blockIdx.x * kProbeThreads + threadIdx.x] = s;
+}
+
+constexpr int kCopyUnroll = 8;
+
+__global__ __launch_bounds__(kProbeThreads) void probe_copy(u32x4* __restrict__ dst, const u32x4* __restrict__ src,
+                                                           int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * kProbeThreads;
+  for (int64_t i0 = (int64_t)blockIdx.x * kProbeThreads + threadIdx.x; i0 < n; i0 += stride * kCopyUnroll) {
+    u32x4 v[kCopyUnroll];
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u)
+      if (i0 + u * stride < n) v[u] = __builtin_nontemporal_load(src + i0 + u * stride);
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u)
+      if (i0 + u * stride < n) __builtin_nontemporal_store(v[u], dst + i0 + u * stride);
+  }
+}
+
+}  // namespace
+
+int probe_grid(int n_cu) { return 2 * n_cu; }
+
+hipError_t launch_probe(int kind, int64_t iters, void* dst, const void* src, size_t n_bytes, int n_cu,
+                        hipStream_t stream, double* work) {
+  const unsigned grid = (unsigned)probe_grid(n_cu);
+  const double waves = (double)grid * (kProbeThreads / 64);
+  switch (kind) {
+    case 0:
+      hipLaunchKernelGGL(probe_mfma, dim3(grid), dim3(kProbeThreads), 0, stream, (float*)dst, iters);
+      *work = waves * (double)iters * 4.0 * 32768.0;                  // flops
+      break;
+    case 1:
+      hipLaunchKernelGGL(probe_valu, dim3(grid), dim3(kProbeThreads), 0, stream, (float*)dst, iters, 0.125f,
+                         -0.5f);
+      *work = (double)grid * kProbeThreads * (double)iters * 16.0;   // elements
+      break;
+    case 2: {
+      const int64_t n = (int64_t)(n_bytes / 16);
+      const unsigned g = (unsigned)(16 * n_cu);
+      hipLaunchKernelGGL(probe_copy, dim3(g), dim3(kProbeThreads), 0, stream, (u32x4*)dst, (const u32x4*)src, n);
+      *work = 2.0 * (double)n * 16.0;                                 // bytes read + written
+      break;
+    }
+    case 3:
+      hipLaunchKernelGGL(probe_mix, dim3(grid), dim3(kProbeThreads), 0, stream, (float*)dst, iters, 1e-6f, -0.5f);
+      *work = waves * (double)iters * 2.0 * 2048.0;                   // logits (2 * 128 MFMA flops each)
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kara

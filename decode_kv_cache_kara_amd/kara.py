@@ -109,6 +109,8 @@ _SIGS = {
     "kara_decode_attention": (_I, [_P, _I, _I, _P, _P, _I, _P, _I, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "kara_sim_gen_length": (_I, [_P, _I]),
     "kara_policy_sim": (_I, [_P, _P, _P, _P, _P]),
+    "kara_probe_scratch_bytes": (ctypes.c_size_t, []),
+    "kara_probe": (_I, [_I, ctypes.c_int64, _P, _P, ctypes.c_size_t, _P, ctypes.POINTER(ctypes.c_double)]),
 }
 EXPORTED = tuple(_SIGS)
 
@@ -392,3 +394,22 @@ def kara_policy_sim(cfg):
     summary = {name: getattr(r, name) for name, _ in kara_sim_result._fields_}
     steps = [(act[i], comp[i], ms[i]) for i in range(r.steps)]
     return summary, steps
+
+
+KARA_PROBE_MFMA = 0
+KARA_PROBE_VALU = 1
+KARA_PROBE_COPY = 2
+KARA_PROBE_MIX = 3
+
+
+def kara_probe_scratch_bytes():
+    return int(_lib.kara_probe_scratch_bytes())
+
+
+def kara_probe(kind, iters, dst, src=None, stream=None):
+    """Enqueues one measurement probe (see include/kara.h); returns its work
+    (flops, elements, bytes read + written, or logits by kind)."""
+    work = ctypes.c_double(0.0)
+    _check(_lib.kara_probe(int(kind), int(iters), _dev(dst, "dst"), None if src is None else _dev(src, "src"),
+                           dst.numel() * dst.element_size(), _stream(stream), ctypes.byref(work)))
+    return work.value

@@ -407,6 +407,34 @@ kara_status kara_policy_sim(const kara_sim_config* config, kara_sim_result* resu
                             int32_t* active_per_step, int32_t* compressions_per_step,
                             double* ms_per_step);
 
+/* ---- Measurement aid: the chip's own ceilings ----------------------------
+ * Not part of the compression step.  A fully loaded MI355X runs below the
+ * clock its nominal peaks assume, so the benchmark sets each kernel's rate
+ * against what this device reaches for the same kind of work:
+ *   KARA_PROBE_MFMA  matrix cores alone: independent chains of 32x32x16 bf16
+ *                    MFMAs, operands in registers; work in flops.
+ *   KARA_PROBE_VALU  the scoring kernel's per-logit VALU work alone (one
+ *                    multiply-add, one exp2, one add per element); work in
+ *                    elements.
+ *   KARA_PROBE_COPY  a streaming copy of n_bytes from src_d to dst_d with
+ *                    16-byte nontemporal loads and stores; work in bytes read
+ *                    plus bytes written.
+ *   KARA_PROBE_MIX   MFMA and VALU work interleaved in one wave in the ratio
+ *                    and order of the scoring kernel's inner loop (2 * 128
+ *                    bf16 MFMA flops and one multiply-add, exp2 and add per
+ *                    logit); work in logits.
+ * MFMA, VALU and MIX run `iters` loop iterations in each of two waves per
+ * SIMD and write one float per thread to dst_d, which must hold
+ * kara_probe_scratch_bytes() bytes (n_bytes gives its size).  COPY ignores
+ * iters; n_bytes and both addresses must be multiples of 16.  The launch is
+ * enqueued on `stream` (the caller times it, e.g. with events); *work_out
+ * receives the launch's work in the unit above.  KARA_E_INVAL on bad
+ * arguments (nothing launched). */
+enum { KARA_PROBE_MFMA = 0, KARA_PROBE_VALU = 1, KARA_PROBE_COPY = 2, KARA_PROBE_MIX = 3 };
+size_t kara_probe_scratch_bytes(void);
+kara_status kara_probe(int32_t kind, int64_t iters, void* dst_d, const void* src_d, size_t n_bytes, void* stream,
+                       double* work_out);
+
 #ifdef __cplusplus
 }
 #endif

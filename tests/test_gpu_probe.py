@@ -1,0 +1,55 @@
+"""The measurement probes behind kara_probe (include/kara.h): the copy probe
+moves the bytes it claims, the loop probes report the work their launch
+shapes imply and finish with finite results, and bad arguments are rejected
+before anything is launched."""
+
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def kara():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    from decode_kv_cache_kara_amd import kara as k
+    return k
+
+
+def test_copy_probe_moves_bytes(kara):
+    n = (1 << 20) + 48                      # not a multiple of one pass of the grid
+    src = torch.randint(0, 255, (n,), dtype=torch.uint8, device="cuda")
+    dst = torch.zeros_like(src)
+    work = kara.kara_probe(kara.KARA_PROBE_COPY, 1, dst, src=src)
+    torch.cuda.synchronize()
+    assert work == 2.0 * n
+    assert torch.equal(dst, src)
+
+
+@pytest.mark.parametrize("kind", [0, 1, 3])
+def test_loop_probes(kara, kind):
+    scratch = torch.full((kara.kara_probe_scratch_bytes() // 4,), float("nan"), device="cuda")
+    iters = 7
+    work = kara.kara_probe(kind, iters, scratch)
+    torch.cuda.synchronize()
+    n_threads = scratch.numel()             # one float per thread of the launch
+    per_wave = {0: iters * 4 * 32768.0, 1: None, 3: iters * 2 * 2048.0}[kind]
+    if kind == 1:
+        assert work == n_threads * iters * 16.0
+    else:
+        assert work == (n_threads / 64) * per_wave
+    assert torch.isfinite(scratch).all()
+
+
+def test_probe_rejects_bad_arguments(kara):
+    scratch = torch.empty(kara.kara_probe_scratch_bytes() // 4, device="cuda")
+    with pytest.raises(kara.KaraError):
+        kara.kara_probe(9, 1, scratch)
+    with pytest.raises(kara.KaraError):
+        kara.kara_probe(kara.KARA_PROBE_MFMA, 0, scratch)
+    with pytest.raises(kara.KaraError):
+        kara.kara_probe(kara.KARA_PROBE_MIX, 1, scratch[:16])
+    odd = torch.zeros(17, dtype=torch.uint8, device="cuda")
+    with pytest.raises(kara.KaraError):
+        kara.kara_probe(kara.KARA_PROBE_COPY, 1, odd, src=odd.clone())
