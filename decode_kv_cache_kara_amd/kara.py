@@ -410,6 +410,8 @@ def kara_probe(kind, iters, dst, src=None, stream=None):
     """Enqueues one measurement probe (see include/kara.h); returns its work
     (flops, elements, bytes read + written, or logits by kind)."""
     work = ctypes.c_double(0.0)
+    if src is not None and src.numel() * src.element_size() < dst.numel() * dst.element_size():
+        raise ValueError("src is smaller than dst")
     _check(_lib.kara_probe(int(kind), int(iters), _dev(dst, "dst"), None if src is None else _dev(src, "src"),
                            dst.numel() * dst.element_size(), _stream(stream), ctypes.byref(work)))
     return work.value

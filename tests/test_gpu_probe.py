@@ -50,6 +50,9 @@ def test_probe_rejects_bad_arguments(kara):
         kara.kara_probe(kara.KARA_PROBE_MFMA, 0, scratch)
     with pytest.raises(kara.KaraError):
         kara.kara_probe(kara.KARA_PROBE_MIX, 1, scratch[:16])
+    with pytest.raises(ValueError):
+        kara.kara_probe(kara.KARA_PROBE_COPY, 1, torch.zeros(64, dtype=torch.uint8, device="cuda"),
+                        src=torch.zeros(32, dtype=torch.uint8, device="cuda"))
     odd = torch.zeros(17, dtype=torch.uint8, device="cuda")
     with pytest.raises(kara.KaraError):
         kara.kara_probe(kara.KARA_PROBE_COPY, 1, odd, src=odd.clone())
