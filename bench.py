@@ -11,6 +11,9 @@ resident in HBM.  Prints one JSON line:
              its duration is measured with HIP events recorded on the call's
              stream around that kernel inside the timed steps
   cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
+                on all host threads (cpu_baseline_1core: one thread, smaller sample)
+  measured_ceilings  the chip's own MFMA, VALU, interleaved and copy rates from
+                the library's probes, and the kernels' times against them
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
 """
@@ -56,7 +59,7 @@ def read_traffic(workload):
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(cfg, n_layers_sample, seed, n_seqs_sample=3, flags=0):
+def cpu_baseline(cfg, n_layers_sample, seed, n_seqs_sample=3, flags=0, one_core=False):
     """Oracle compress() on n_seqs_sample sequences x n_layers_sample layers of
     the same shapes, extrapolated to the metric's unit (window tokens of the
     full model slice per second)."""
@@ -73,13 +76,16 @@ def cpu_baseline(cfg, n_layers_sample, seed, n_seqs_sample=3, flags=0):
     pool = wl.pool.to(torch.float64).numpy()
     table = wl.table.long().numpy()
     lens = wl.lens.long().numpy()
-    t0 = time.perf_counter()
-    ko.compress(q, pool, table, lens, wl.window, wl.protect, wl.top_k, wl.budget, wl.block_size,
-                wl.free_ids, unidirectional=bool(flags & 1), chunks=not (flags & 2))
-    dt = time.perf_counter() - t0
+    from threadpoolctl import threadpool_limits
+
+    with threadpool_limits(limits=1 if one_core else None):
+        t0 = time.perf_counter()
+        ko.compress(q, pool, table, lens, wl.window, wl.protect, wl.top_k, wl.budget, wl.block_size,
+                    wl.free_ids, unidirectional=bool(flags & 1), chunks=not (flags & 2))
+        dt = time.perf_counter() - t0
     frac = n_layers_sample / full["n_layers"]
     value = n_seqs_sample * wl.window * frac / dt
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    threads = 1 if one_core else max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     return {"value": value, "unit": "window tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": (f"oracle compress() (fp64 scores, Top-K, Token2Chunk, pool plan, row gather) on "
                        f"{n_seqs_sample} sequences x {n_layers_sample} of {full['n_layers']} layers of the same "
@@ -434,6 +440,9 @@ def main():
         n_layers_sample = min(args.cpu_layers, synth.CONFIGS[args.config]["n_layers"])
         out["cpu_baseline"] = cpu_baseline(args.config, n_layers_sample, seed=7, flags=args.flags)
         log(f"cpu baseline {out['cpu_baseline']['value']:.1f} window tokens/s")
+        out["cpu_baseline_1core"] = cpu_baseline(args.config, min(8, n_layers_sample), seed=7, n_seqs_sample=1,
+                                                 flags=args.flags, one_core=True)
+        log(f"cpu baseline on one core {out['cpu_baseline_1core']['value']:.1f} window tokens/s")
     print(json.dumps(out), flush=True)
 
 
