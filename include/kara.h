@@ -428,8 +428,11 @@ kara_status kara_policy_sim(const kara_sim_config* config, kara_sim_result* resu
  * kara_probe_scratch_bytes() bytes (n_bytes gives its size).  COPY ignores
  * iters; n_bytes and both addresses must be multiples of 16.  The launch is
  * enqueued on `stream` (the caller times it, e.g. with events); *work_out
- * receives the launch's work in the unit above.  KARA_E_INVAL on bad
- * arguments (nothing launched). */
+ * receives the launch's work in the unit above.  dst_d and src_d are
+ * caller-owned device buffers; src_d must hold n_bytes.  KARA_E_INVAL on bad
+ * arguments (nothing launched); KARA_E_HIP when there is no current device or
+ * the launch fails.  kara_probe_scratch_bytes() returns 0 when there is no
+ * current device. */
 enum { KARA_PROBE_MFMA = 0, KARA_PROBE_VALU = 1, KARA_PROBE_COPY = 2, KARA_PROBE_MIX = 3 };
 size_t kara_probe_scratch_bytes(void);
 kara_status kara_probe(int32_t kind, int64_t iters, void* dst_d, const void* src_d, size_t n_bytes, void* stream,
