@@ -121,9 +121,43 @@ __device__ __forceinline__ void segment(int n, int* j0, int* j1) {
 // (ties to the lower position).  Requires 1 <= n <= number of free positions.
 __device__ void select_largest(SelectShared& sh, int C, int n, uint8_t tag) {
   const int tid = threadIdx.x;
-  uint32_t prefix = 0u, mask = 0u;
+  // The keys of the free positions agree on every bit above the highest bit in
+  // which their largest and smallest differ, so the digit passes start at the
+  // digit that holds that bit: a pass above it would put every key in one bin
+  // (and spend its time on one contended LDS counter).
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+  for (int j = tid; j < C; j += kThreads) {
+    if (sh.state[j] == kFree) {
+      const uint32_t k = sh.key[j];
+      kmin = k < kmin ? k : kmin;
+      kmax = k > kmax ? k : kmax;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint32_t a = __shfl_xor(kmin, o), b = __shfl_xor(kmax, o);
+    kmin = a < kmin ? a : kmin;
+    kmax = b > kmax ? b : kmax;
+  }
+  uint32_t* scratch = (uint32_t*)sh.hist;
+  if ((tid & 63) == 0) {
+    scratch[2 * (tid >> 6)] = kmin;
+    scratch[2 * (tid >> 6) + 1] = kmax;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const uint32_t a = scratch[2 * w], b = scratch[2 * w + 1];
+    kmin = a < kmin ? a : kmin;
+    kmax = b > kmax ? b : kmax;
+  }
+  __syncthreads();
+  const uint32_t diff = kmin ^ kmax;
+  const int top = diff == 0u ? -8 : (31 - __clz(diff)) / 8 * 8;   // -8: all free keys are equal
+  uint32_t mask = top >= 24 ? 0u : ~((1u << (top + 8)) - 1u);
+  uint32_t prefix = kmax & mask;
   int remaining = n;
-  for (int shift = 24; shift >= 0; shift -= 8) {
+  for (int shift = top; shift >= 0; shift -= 8) {
     for (int i = tid; i < 256; i += kThreads) sh.hist[i] = 0;
     __syncthreads();
     for (int j = tid; j < C; j += kThreads) {
