@@ -1,10 +1,12 @@
-// Top-K candidate selection and Token2Chunk, one workgroup per unit.
+// Top-K candidate selection and Token2Chunk, one wave per unit.
 //
-// Scores live in LDS as float32 and as order-preserving 32-bit keys.  Both
-// selections (the K candidates; the top-up of the budget) are exact radix
-// selects over the keys (four 8-bit digit passes with an LDS histogram), with
-// ties at the threshold resolved by position through a block-wide prefix count,
-// so the results are the "largest score, lower position first" sets bit for bit
+// The unit's scores are the chunk-ordered sums of the scoring kernel's partial
+// column sums.  Both selections (the K candidates; the top-up of the budget)
+// are exact radix selects over order-preserving 32-bit keys: from the highest
+// bit in which the eligible keys differ down, the threshold key is fixed one
+// bit at a time by counting matching keys with wave ballots, and keys equal to
+// the threshold are taken in position order through a wave prefix count, so
+// the results are the "largest score, lower position first" sets bit for bit
 // ("Technical Summary: Kara", Methodology 1, Selection).
 //
 // Token2Chunk ("Technical Summary: Kara", Methodology 2, Process and Outcome;
@@ -27,52 +29,6 @@
 namespace kara {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
-
-enum : uint8_t { kFree = 0, kCand = 1, kSpan = 2, kTopUp = 3 };
-
-// LDS of one workgroup, carved from dynamic shared memory sized by the call:
-// per position of the region its score, order key and state; per candidate
-// (or span between consecutive candidates) the candidate position, chunk
-// score, gap, rank and ranked gap; and small scratch.
-struct SelectShared {
-  float* s;           // [C]
-  uint32_t* key;      // [C]
-  uint8_t* state;     // [C]
-  int* cand;          // [K]
-  float* sigma;       // [K]
-  int* gap;           // [K]
-  int* ordgap;        // [K] gaps in rank order, then their inclusive prefix sums
-  int* rank;          // [K]
-  int* hist;          // [256]
-  int* scan_tmp;      // [kWaves]
-  int* misc;          // [4]
-};
-
-__host__ __device__ inline size_t select_lds_bytes(int C, int K) {
-  const size_t c4 = (size_t)C * 4, k4 = (size_t)K * 4;
-  return 2 * c4 + ((size_t)C + 3) / 4 * 4 + 5 * k4 + (256 + kWaves + 4) * 4;
-}
-
-__device__ inline SelectShared carve(char* base, int C, int K) {
-  SelectShared sh;
-  char* p = base;
-  auto take = [&](size_t n) { char* q = p; p += (n + 3) / 4 * 4; return q; };
-  sh.s = (float*)take((size_t)C * 4);
-  sh.key = (uint32_t*)take((size_t)C * 4);
-  sh.state = (uint8_t*)take((size_t)C);
-  sh.cand = (int*)take((size_t)K * 4);
-  sh.sigma = (float*)take((size_t)K * 4);
-  sh.gap = (int*)take((size_t)K * 4);
-  sh.ordgap = (int*)take((size_t)K * 4);
-  sh.rank = (int*)take((size_t)K * 4);
-  sh.hist = (int*)take(256 * 4);
-  sh.scan_tmp = (int*)take(kWaves * 4);
-  sh.misc = (int*)take(4 * 4);
-  return sh;
-}
-
 __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f);
   if (u == 0x80000000u) u = 0u;  // -0 ranks as +0
@@ -89,48 +45,84 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
-// Exclusive prefix of v over threads in index order; *total = sum over all.
-__device__ int block_excl_scan(int v, SelectShared& sh, int* total) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int inc = wave_incl_scan(v);
-  if (lane == 63) sh.scan_tmp[w] = inc;
-  __syncthreads();
-  int off = 0, tot = 0;
+// ---------------------------------------------------------------------------
+// One wave per unit.  Lane l owns the contiguous positions [l*P, l*P + P) of
+// the region (P = ceil(C / 64)), so position order is (lane, slot) order and
+// prefix counts are wave scans.  The order keys of a lane's positions stay in
+// registers and the marks of its positions in bit masks (bit i = slot i);
+// the scores, a flag per position, and per candidate or span the position,
+// chunk score, gap, rank and ranked gap live in the wave's part of LDS.
+// There is no workgroup barrier: the waves of a workgroup score different
+// units, and a wave orders its own LDS accesses with a wavefront fence.
+// ---------------------------------------------------------------------------
+
+constexpr int kSelWaves = 4;   // units per workgroup when LDS allows
+
+struct WaveShared {
+  float* s;         // [C]
+  uint8_t* flag;    // [C]
+  int* cand;        // [K]
+  float* sigma;     // [K]
+  int* gap;         // [K]
+  int* rank;        // [K]
+  int* ordgap;      // [K]
+};
+
+__host__ __device__ inline size_t wave_lds_bytes(int C, int K) {
+  return (size_t)C * 4 + ((size_t)C + 3) / 4 * 4 + (size_t)K * 20;
+}
+
+__device__ inline WaveShared carve_wave(char* base, int C, int K) {
+  WaveShared sh;
+  char* p = base;
+  auto take = [&](size_t n) { char* q = p; p += (n + 3) / 4 * 4; return q; };
+  sh.s = (float*)take((size_t)C * 4);
+  sh.flag = (uint8_t*)take((size_t)C);
+  sh.cand = (int*)take((size_t)K * 4);
+  sh.sigma = (float*)take((size_t)K * 4);
+  sh.gap = (int*)take((size_t)K * 4);
+  sh.rank = (int*)take((size_t)K * 4);
+  sh.ordgap = (int*)take((size_t)K * 4);
+  return sh;
+}
+
+// Makes this wave's earlier LDS writes visible to its later LDS reads.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+__device__ __forceinline__ int wave_max(int v) {
 #pragma unroll
-  for (int i = 0; i < kWaves; ++i) {
-    const int x = sh.scan_tmp[i];
-    if (i < w) off += x;
-    tot += x;
+  for (int o = 32; o > 0; o >>= 1) {
+    const int t = __shfl_xor(v, o);
+    v = t > v ? t : v;
   }
-  __syncthreads();
-  *total = tot;
-  return off + inc - v;
+  return v;
 }
 
-// Contiguous segment of [0, n) owned by this thread (prefix scans run in
-// position order).
-__device__ __forceinline__ void segment(int n, int* j0, int* j1) {
-  const int per = (n + kThreads - 1) / kThreads;
-  int a = threadIdx.x * per;
-  int b = a + per;
-  *j0 = a < n ? a : n;
-  *j1 = b < n ? b : n;
+// Exclusive prefix over lanes; *total = sum over the wave.
+__device__ __forceinline__ int wave_excl(int v, int* total) {
+  const int inc = wave_incl_scan(v);
+  *total = __shfl(inc, 63);
+  return inc - v;
 }
 
-// Marks with `tag` the n largest-key positions among those in state kFree
-// (ties to the lower position).  Requires 1 <= n <= number of free positions.
-__device__ void select_largest(SelectShared& sh, int C, int n, uint8_t tag) {
-  const int tid = threadIdx.x;
-  // The keys of the free positions agree on every bit above the highest bit in
-  // which their largest and smallest differ, so the digit passes start at the
-  // digit that holds that bit: a pass above it would put every key in one bin
-  // (and spend its time on one contended LDS counter).
+// Marks (returned bit mask) of the n largest keys among the lane slots in
+// `elig` over the wave, ties to the lower position.  Requires 1 <= n <= the
+// number of eligible slots.  Bitwise radix select: from the highest bit in
+// which the eligible keys differ down, the n-th largest key T is fixed one bit
+// at a time by counting (ballots) the keys that match T so far and have the
+// bit set; then every eligible key above T is taken and the keys equal to T
+// are taken in position order up to n.
+template <int kP>
+__device__ uint32_t wave_select(const uint32_t* key, uint32_t elig, int n) {
   uint32_t kmin = 0xffffffffu, kmax = 0u;
-  for (int j = tid; j < C; j += kThreads) {
-    if (sh.state[j] == kFree) {
-      const uint32_t k = sh.key[j];
-      kmin = k < kmin ? k : kmin;
-      kmax = k > kmax ? k : kmax;
+#pragma unroll
+  for (int i = 0; i < kP; ++i) {
+    if ((elig >> i) & 1u) {
+      kmin = key[i] < kmin ? key[i] : kmin;
+      kmax = key[i] > kmax ? key[i] : kmax;
     }
   }
 #pragma unroll
@@ -139,262 +131,244 @@ __device__ void select_largest(SelectShared& sh, int C, int n, uint8_t tag) {
     kmin = a < kmin ? a : kmin;
     kmax = b > kmax ? b : kmax;
   }
-  uint32_t* scratch = (uint32_t*)sh.hist;
-  if ((tid & 63) == 0) {
-    scratch[2 * (tid >> 6)] = kmin;
-    scratch[2 * (tid >> 6) + 1] = kmax;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    const uint32_t a = scratch[2 * w], b = scratch[2 * w + 1];
-    kmin = a < kmin ? a : kmin;
-    kmax = b > kmax ? b : kmax;
-  }
-  __syncthreads();
   const uint32_t diff = kmin ^ kmax;
-  const int top = diff == 0u ? -8 : (31 - __clz(diff)) / 8 * 8;   // -8: all free keys are equal
-  uint32_t mask = top >= 24 ? 0u : ~((1u << (top + 8)) - 1u);
-  uint32_t prefix = kmax & mask;
+  uint32_t prefix = kmax, hm = 0xffffffffu;
   int remaining = n;
-  for (int shift = top; shift >= 0; shift -= 8) {
-    for (int i = tid; i < 256; i += kThreads) sh.hist[i] = 0;
-    __syncthreads();
-    for (int j = tid; j < C; j += kThreads) {
-      if (sh.state[j] == kFree) {
-        const uint32_t k = sh.key[j];
-        if ((k & mask) == prefix) atomicAdd(&sh.hist[(k >> shift) & 255u], 1);
-      }
+  if (diff != 0u) {
+    const int hb = 31 - __clz((int)diff);
+    hm = ~((2u << hb) - 1u);                       // the bits above hb (none for hb = 31)
+    prefix = kmax & hm;
+    for (int b = hb; b >= 0; --b) {
+      const uint32_t bit = 1u << b;
+      int cnt = 0;
+#pragma unroll
+      for (int i = 0; i < kP; ++i)
+        cnt += __popcll(__ballot(((elig >> i) & 1u) && (key[i] & hm) == prefix && (key[i] & bit)));
+      if (cnt >= remaining) prefix |= bit;
+      else remaining -= cnt;
+      hm |= bit;
     }
-    __syncthreads();
-    if (tid < 64) {
-      // lane l holds digits 255-4l .. 252-4l; counts accumulate from the top digit down
-      const int d0 = 255 - 4 * tid;
-      const int c0 = sh.hist[d0], c1 = sh.hist[d0 - 1], c2 = sh.hist[d0 - 2], c3 = sh.hist[d0 - 3];
-      const int s = c0 + c1 + c2 + c3;
-      const int inc = wave_incl_scan(s);
-      const int before = inc - s;
-      if (before < remaining && remaining <= inc) {
-        int acc = before, d;
-        if (acc + c0 >= remaining) {
-          d = d0;
-        } else if ((acc += c0) + c1 >= remaining) {
-          d = d0 - 1;
-        } else if ((acc += c1) + c2 >= remaining) {
-          d = d0 - 2;
-        } else {
-          acc += c2;
-          d = d0 - 3;
-        }
-        sh.misc[0] = d;
-        sh.misc[1] = acc;
-      }
-    }
-    __syncthreads();
-    remaining -= sh.misc[1];
-    prefix |= (uint32_t)sh.misc[0] << shift;
-    mask |= 255u << shift;
-    __syncthreads();
   }
-  // prefix is the key of the n-th largest; take `remaining` of the keys equal
-  // to it, lowest positions first.
-  const uint32_t T = prefix;
-  int j0, j1;
-  segment(C, &j0, &j1);
-  int eq = 0;
-  for (int j = j0; j < j1; ++j) eq += (sh.state[j] == kFree && sh.key[j] == T);
+  uint32_t sel = 0u, eq = 0u;
+#pragma unroll
+  for (int i = 0; i < kP; ++i) {
+    if ((elig >> i) & 1u) {
+      if (key[i] > prefix) sel |= 1u << i;
+      else if (key[i] == prefix) eq |= 1u << i;
+    }
+  }
   int tot;
-  int before = block_excl_scan(eq, sh, &tot);
-  for (int j = j0; j < j1; ++j) {
-    if (sh.state[j] != kFree) continue;
-    const uint32_t k = sh.key[j];
-    if (k > T) {
-      sh.state[j] = tag;
-    } else if (k == T) {
-      if (before < remaining) sh.state[j] = tag;
+  int before = wave_excl(__popc(eq), &tot);
+#pragma unroll
+  for (int i = 0; i < kP; ++i) {
+    if ((eq >> i) & 1u) {
+      if (before < remaining) sel |= 1u << i;
       ++before;
     }
   }
-  __syncthreads();
+  return sel;
 }
 
-// Writes the ascending positions whose state satisfies `pred` to out[0..cap).
-template <typename P>
-__device__ int write_positions(SelectShared& sh, int C, P pred, int32_t* out, int cap) {
-  int j0, j1;
-  segment(C, &j0, &j1);
-  int cnt = 0;
-  for (int j = j0; j < j1; ++j) cnt += pred(sh.state[j]) ? 1 : 0;
+// Writes the ascending positions marked in `m` to out[0..cap).
+template <int kP>
+__device__ void wave_write(uint32_t m, int j0, int32_t* out, int cap) {
   int tot;
-  int off = block_excl_scan(cnt, sh, &tot);
-  for (int j = j0; j < j1; ++j)
-    if (pred(sh.state[j])) {
-      if (off < cap) out[off] = j;
+  int off = wave_excl(__popc(m), &tot);
+#pragma unroll
+  for (int i = 0; i < kP; ++i) {
+    if ((m >> i) & 1u) {
+      if (off < cap) out[off] = j0 + i;
       ++off;
     }
-  __syncthreads();
-  return tot;
+  }
 }
 
-__device__ void clear_state(SelectShared& sh, int C) {
-  for (int j = threadIdx.x; j < C; j += kThreads) sh.state[j] = kFree;
-  __syncthreads();
-}
+template <int kP>
+__global__ __launch_bounds__(64 * kSelWaves) void select_wave_kernel(SelectArgs a, size_t wave_bytes) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int unit = blockIdx.x * (int)(blockDim.x >> 6) + wave;
+  if (unit >= a.n_units) return;                  // per wave: no workgroup barriers below
+  const int C = a.C, K = a.K, R = a.R;
+  WaveShared sh = carve_wave(smem + (size_t)wave * wave_bytes, C, K);
+  const int P = (C + 63) / 64;
+  const int j0 = lane * P;
+  const int nmine = C - j0 < 0 ? 0 : (C - j0 > P ? P : C - j0);
+  const uint32_t valid = nmine >= 32 ? 0xffffffffu : ((1u << nmine) - 1u);
 
-// Token2Chunk from candidates marked kCand; leaves kCand/kSpan/kTopUp marks on
-// exactly R positions.
-__device__ void token2chunk(SelectShared& sh, int C, int R) {
-  const int tid = threadIdx.x;
-  // ascending candidate list, and each thread's count of candidates before its segment
-  int j0, j1;
-  segment(C, &j0, &j1);
-  int cnt = 0;
-  for (int j = j0; j < j1; ++j) cnt += (sh.state[j] == kCand);
-  int K;
-  const int cbefore = block_excl_scan(cnt, sh, &K);
-  {
-    int o = cbefore;
-    for (int j = j0; j < j1; ++j)
-      if (sh.state[j] == kCand) sh.cand[o++] = j;
-  }
-  __syncthreads();
-  if (R <= K) return;  // budget already met by the candidates
-
-  // spans between consecutive candidates
-  const int nspan = K - 1;
-  for (int m = tid; m < nspan; m += kThreads) {
-    const int a = sh.cand[m], b = sh.cand[m + 1];
-    const int g = b - a - 1;
-    sh.gap[m] = g;
-    sh.sigma[m] = g > 0 ? __fdiv_rn(__fadd_rn(sh.s[a], sh.s[b]), (float)(g + 2)) : 0.0f;
-  }
-  __syncthreads();
-  // rank among spans with a gap: (sigma desc, left endpoint asc)
-  for (int m = tid; m < nspan; m += kThreads) {
-    if (sh.gap[m] == 0) {
-      sh.rank[m] = -1;
-      continue;
+  // unit scores: the partial sums of the row chunks added in chunk order.
+  // Four positions and eight chunks are loaded at a time (32 loads in flight
+  // per lane) before any is added, so the wave waits once per batch rather
+  // than once per load.
+  const float* pp = a.partials + (size_t)unit * a.n_split * C;
+  constexpr int kJ = 4, kKb = 8;
+  for (int jb = 0; jb < C; jb += 64 * kJ) {
+    float acc[kJ];
+#pragma unroll
+    for (int u = 0; u < kJ; ++u) acc[u] = 0.0f;
+    for (int k0 = 0; k0 < a.n_split; k0 += kKb) {
+      float v[kJ][kKb];
+#pragma unroll
+      for (int u = 0; u < kJ; ++u) {
+        const int j = jb + lane + 64 * u;
+#pragma unroll
+        for (int kk = 0; kk < kKb; ++kk)
+          v[u][kk] = (j < C && k0 + kk < a.n_split) ? pp[(size_t)(k0 + kk) * C + j] : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < kJ; ++u)
+#pragma unroll
+        for (int kk = 0; kk < kKb; ++kk)
+          if (k0 + kk < a.n_split) acc[u] += v[u][kk];
     }
-    const float sm = sh.sigma[m];
-    int r = 0;
-    for (int o = 0; o < nspan; ++o) {
-      if (sh.gap[o] == 0) continue;
-      const float so = sh.sigma[o];
-      r += (so > sm || (so == sm && o < m)) ? 1 : 0;
-    }
-    sh.rank[m] = r;
-  }
-  __syncthreads();
-  int nvalid_local = 0;
-  for (int m = tid; m < nspan; m += kThreads) {
-    if (sh.rank[m] >= 0) {
-      sh.ordgap[sh.rank[m]] = sh.gap[m];
-      ++nvalid_local;
-    }
-  }
-  __syncthreads();
-  int nvalid;
-  {
-    int dummy = block_excl_scan(nvalid_local, sh, &nvalid);
-    (void)dummy;
-  }
-  // inclusive prefix of the gaps in rank order
-  {
-    int a0, a1;
-    segment(nvalid, &a0, &a1);
-    int sum = 0;
-    for (int r = a0; r < a1; ++r) sum += sh.ordgap[r];
-    int tot;
-    int run = block_excl_scan(sum, sh, &tot);
-    for (int r = a0; r < a1; ++r) {
-      run += sh.ordgap[r];
-      sh.ordgap[r] = run;
-    }
-  }
-  __syncthreads();
-  const int room = R - K;
-  // accepted spans mark their interiors; span m holds the non-candidates whose
-  // candidate count so far is m + 1
-  {
-    int seen = cbefore;
-    for (int j = j0; j < j1; ++j) {
-      if (sh.state[j] == kCand) {
-        ++seen;
-      } else if (seen >= 1 && seen <= nspan) {
-        const int r = sh.rank[seen - 1];
-        if (r >= 0 && sh.ordgap[r] <= room) sh.state[j] = kSpan;
+#pragma unroll
+    for (int u = 0; u < kJ; ++u) {
+      const int j = jb + lane + 64 * u;
+      if (j < C) {
+        sh.s[j] = acc[u];
+        sh.flag[j] = 0;
+        if (a.scores_out) a.scores_out[(size_t)unit * C + j] = acc[u];
       }
     }
   }
-  // tokens added by the accepted spans = the largest accepted prefix sum
-  int used_local = 0;
-  for (int m = tid; m < nspan; m += kThreads) {
-    const int r = sh.rank[m];
-    if (r >= 0 && sh.ordgap[r] <= room && sh.ordgap[r] > used_local) used_local = sh.ordgap[r];
-  }
-  // block max through the histogram scratch
-  if (tid == 0) sh.misc[2] = 0;
-  __syncthreads();
-  atomicMax(&sh.misc[2], used_local);
-  __syncthreads();
-  const int need = room - sh.misc[2];
-  __syncthreads();
-  if (need > 0) select_largest(sh, C, need, kTopUp);
-}
+  wave_sync();
+  uint32_t key[kP];
+#pragma unroll
+  for (int i = 0; i < kP; ++i) key[i] = i < nmine ? order_key(sh.s[j0 + i]) : 0u;
 
-__global__ __launch_bounds__(kThreads) void select_kernel(SelectArgs a) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-  SelectShared sh = carve(smem, a.C, a.K);
-  const int unit = blockIdx.x;
-  const int C = a.C, K = a.K, R = a.R;
-  const int tid = threadIdx.x;
-
-  const float* p = a.partials + (size_t)unit * a.n_split * C;
-  for (int j = tid; j < C; j += kThreads) {
-    float s = 0.0f;
-    for (int k = 0; k < a.n_split; ++k) s += p[(size_t)k * C + j];
-    sh.s[j] = s;
-    sh.key[j] = order_key(s);
-    sh.state[j] = kFree;
-    if (a.scores_out) a.scores_out[(size_t)unit * C + j] = s;
-  }
-  __syncthreads();
-
+  uint32_t cand;
   if (a.mode == kSelectT2C) {
     const int32_t* ci = a.cand_in + (size_t)unit * K;
-    for (int m = tid; m < K; m += kThreads) {
+    for (int m = lane; m < K; m += 64) {
       int j = ci[m];
       j = j < 0 ? 0 : (j >= C ? C - 1 : j);
-      sh.state[j] = kCand;
+      sh.flag[j] = 1;
     }
-    __syncthreads();
+    wave_sync();
+    cand = 0u;
+#pragma unroll
+    for (int i = 0; i < kP; ++i)
+      if (i < nmine && sh.flag[j0 + i]) cand |= 1u << i;
   } else {
-    select_largest(sh, C, K, kCand);
-    if (a.cand_out) write_positions(sh, C, [](uint8_t st) { return st == kCand; }, a.cand_out + (size_t)unit * K, K);
+    cand = wave_select<kP>(key, valid, K);
+    if (a.cand_out) wave_write<kP>(cand, j0, a.cand_out + (size_t)unit * K, K);
     if (a.mode == kSelectTopK) return;
   }
 
+  uint32_t keep;
   if (R < K) {
-    clear_state(sh, C);
-    select_largest(sh, C, R, kCand);
+    keep = wave_select<kP>(key, valid, R);
   } else if (a.no_chunks) {
-    // Token2Chunk off: the top-R set is the top-K set plus the R - K best of
-    // the rest (one total order: score desc, position asc).
-    if (R > K) select_largest(sh, C, R - K, kTopUp);
+    // Token2Chunk off: the top-K set plus the R - K best of the rest
+    keep = cand | (R > K ? wave_select<kP>(key, valid & ~cand, R - K) : 0u);
   } else {
-    token2chunk(sh, C, R);
+    // Token2Chunk: candidates in ascending order
+    int nc;
+    const int cb = wave_excl(__popc(cand), &nc);
+    {
+      int o = cb;
+#pragma unroll
+      for (int i = 0; i < kP; ++i)
+        if ((cand >> i) & 1u) sh.cand[o++] = j0 + i;
+    }
+    wave_sync();
+    uint32_t span = 0u, topup = 0u;
+    if (R > nc) {
+      const int nspan = nc - 1;
+      for (int m = lane; m < nspan; m += 64) {
+        const int x = sh.cand[m], y = sh.cand[m + 1];
+        const int g = y - x - 1;
+        sh.gap[m] = g;
+        sh.sigma[m] = g > 0 ? __fdiv_rn(__fadd_rn(sh.s[x], sh.s[y]), (float)(g + 2)) : 0.0f;
+      }
+      wave_sync();
+      // rank among spans with a gap: (sigma desc, left endpoint asc)
+      int nvalid_lane = 0;
+      for (int m = lane; m < nspan; m += 64) {
+        int r = -1;
+        if (sh.gap[m] != 0) {
+          const float sm = sh.sigma[m];
+          r = 0;
+          for (int o = 0; o < nspan; ++o) {
+            if (sh.gap[o] == 0) continue;
+            const float so = sh.sigma[o];
+            r += (so > sm || (so == sm && o < m)) ? 1 : 0;
+          }
+          ++nvalid_lane;
+        }
+        sh.rank[m] = r;
+      }
+      wave_sync();
+      for (int m = lane; m < nspan; m += 64)
+        if (sh.rank[m] >= 0) sh.ordgap[sh.rank[m]] = sh.gap[m];
+      int nvalid;
+      (void)wave_excl(nvalid_lane, &nvalid);
+      wave_sync();
+      // inclusive prefix of the gaps in rank order
+      {
+        const int per = (nvalid + 63) / 64;
+        const int a0 = lane * per < nvalid ? lane * per : nvalid;
+        const int a1 = a0 + per < nvalid ? a0 + per : nvalid;
+        int sum = 0;
+        for (int r = a0; r < a1; ++r) sum += sh.ordgap[r];
+        int tot;
+        int run = wave_excl(sum, &tot);
+        for (int r = a0; r < a1; ++r) {
+          run += sh.ordgap[r];
+          sh.ordgap[r] = run;
+        }
+      }
+      wave_sync();
+      const int room = R - nc;
+      // accepted spans mark their interiors: span m holds the non-candidates
+      // whose count of candidates so far is m + 1
+      {
+        int seen = cb;
+#pragma unroll
+        for (int i = 0; i < kP; ++i) {
+          if (i >= nmine) continue;
+          if ((cand >> i) & 1u) {
+            ++seen;
+          } else if (seen >= 1 && seen <= nspan) {
+            const int r = sh.rank[seen - 1];
+            if (r >= 0 && sh.ordgap[r] <= room) span |= 1u << i;
+          }
+        }
+      }
+      // tokens added by the accepted spans = the largest accepted prefix sum
+      int used = 0;
+      for (int m = lane; m < nspan; m += 64) {
+        const int r = sh.rank[m];
+        if (r >= 0 && sh.ordgap[r] <= room && sh.ordgap[r] > used) used = sh.ordgap[r];
+      }
+      used = wave_max(used);
+      const int need = room - used;
+      if (need > 0) topup = wave_select<kP>(key, valid & ~cand & ~span, need);
+    }
+    keep = cand | span | topup;
   }
-  write_positions(sh, C, [](uint8_t st) { return st != kFree; }, a.retained_out + (size_t)unit * R, R);
+  wave_write<kP>(keep, j0, a.retained_out + (size_t)unit * R, R);
 }
 
 }  // namespace
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
   if (a.n_units == 0) return hipSuccess;
-  // at most 2 * 8 KiB + 2 KiB + 5 * 8 KiB + 1 KiB (C = K = 2048): within the
-  // default 64 KiB of dynamic LDS
-  const size_t bytes = select_lds_bytes(a.C, a.K);
-  hipLaunchKernelGGL(select_kernel, dim3(a.n_units), dim3(kThreads), bytes, stream, a);
+  // one wave per unit, as many waves per workgroup as 64 KiB of LDS holds
+  // (at most 3.5 KiB + 0.9 KiB + 20 B per candidate at C = 896, K = 64;
+  // 51 KiB at C = K = 2048)
+  const size_t wave_bytes = (wave_lds_bytes(a.C, a.K) + 15) / 16 * 16;
+  int waves = (int)(65536 / wave_bytes);
+  waves = waves < 1 ? 1 : (waves > kSelWaves ? kSelWaves : waves);
+  const unsigned grid = (unsigned)((a.n_units + waves - 1) / waves);
+  const size_t bytes = wave_bytes * waves;
+  const int P = (a.C + 63) / 64;
+  if (P <= 8)
+    hipLaunchKernelGGL(select_wave_kernel<8>, dim3(grid), dim3(64 * waves), bytes, stream, a, wave_bytes);
+  else if (P <= 16)
+    hipLaunchKernelGGL(select_wave_kernel<16>, dim3(grid), dim3(64 * waves), bytes, stream, a, wave_bytes);
+  else
+    hipLaunchKernelGGL(select_wave_kernel<32>, dim3(grid), dim3(64 * waves), bytes, stream, a, wave_bytes);
   return hipGetLastError();
 }
 
