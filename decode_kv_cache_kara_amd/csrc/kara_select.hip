@@ -26,6 +26,8 @@
 
 #include "kara_internal.hpp"
 
+#include <type_traits>
+
 namespace kara {
 namespace {
 
@@ -108,13 +110,30 @@ __device__ __forceinline__ int wave_excl(int v, int* total) {
   return inc - v;
 }
 
+// Sum of v over the wave (every lane gets it): DPP sums within each row of 16
+// lanes, then the four row sums.
+__device__ __forceinline__ int wave_sum(int v) {
+  auto add_dpp = [](int x, auto ctrl) {
+    return x + __builtin_amdgcn_update_dpp(0, x, decltype(ctrl)::value, 0xF, 0xF, false);
+  };
+  v = add_dpp(v, std::integral_constant<int, 0xB1>());    // quad_perm [1,0,3,2]
+  v = add_dpp(v, std::integral_constant<int, 0x4E>());    // quad_perm [2,3,0,1]
+  v = add_dpp(v, std::integral_constant<int, 0x141>());   // row_half_mirror
+  v = add_dpp(v, std::integral_constant<int, 0x140>());   // row_mirror
+  return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) + __builtin_amdgcn_readlane(v, 32) +
+         __builtin_amdgcn_readlane(v, 48);
+}
+
 // Marks (returned bit mask) of the n largest keys among the lane slots in
 // `elig` over the wave, ties to the lower position.  Requires 1 <= n <= the
 // number of eligible slots.  Bitwise radix select: from the highest bit in
 // which the eligible keys differ down, the n-th largest key T is fixed one bit
-// at a time by counting (ballots) the keys that match T so far and have the
-// bit set; then every eligible key above T is taken and the keys equal to T
-// are taken in position order up to n.
+// at a time.  `live` marks the eligible slots whose key matches T on the bits
+// fixed so far; at each bit the live keys with the bit set are counted over the
+// wave: if there are at least as many as still wanted, T has the bit set and
+// the others leave; otherwise they are all above T, are taken, and leave.
+// The live slots left at the end hold keys equal to T and are taken in
+// position order up to n.
 template <int kP>
 __device__ uint32_t wave_select(const uint32_t* key, uint32_t elig, int n) {
   uint32_t kmin = 0xffffffffu, kmax = 0u;
@@ -132,36 +151,30 @@ __device__ uint32_t wave_select(const uint32_t* key, uint32_t elig, int n) {
     kmax = b > kmax ? b : kmax;
   }
   const uint32_t diff = kmin ^ kmax;
-  uint32_t prefix = kmax, hm = 0xffffffffu;
+  uint32_t live = elig, above = 0u;
   int remaining = n;
   if (diff != 0u) {
-    const int hb = 31 - __clz((int)diff);
-    hm = ~((2u << hb) - 1u);                       // the bits above hb (none for hb = 31)
-    prefix = kmax & hm;
-    for (int b = hb; b >= 0; --b) {
-      const uint32_t bit = 1u << b;
-      int cnt = 0;
+    for (int b = 31 - __clz((int)diff); b >= 0; --b) {
+      uint32_t ones = 0u;                        // slots whose key has bit b set
 #pragma unroll
-      for (int i = 0; i < kP; ++i)
-        cnt += __popcll(__ballot(((elig >> i) & 1u) && (key[i] & hm) == prefix && (key[i] & bit)));
-      if (cnt >= remaining) prefix |= bit;
-      else remaining -= cnt;
-      hm |= bit;
-    }
-  }
-  uint32_t sel = 0u, eq = 0u;
-#pragma unroll
-  for (int i = 0; i < kP; ++i) {
-    if ((elig >> i) & 1u) {
-      if (key[i] > prefix) sel |= 1u << i;
-      else if (key[i] == prefix) eq |= 1u << i;
+      for (int i = 0; i < kP; ++i) ones |= ((key[i] >> b) & 1u) << i;
+      const uint32_t hi = live & ones;
+      const int cnt = wave_sum(__popc(hi));
+      if (cnt >= remaining) {
+        live = hi;
+      } else {
+        above |= hi;
+        live &= ~ones;
+        remaining -= cnt;
+      }
     }
   }
   int tot;
-  int before = wave_excl(__popc(eq), &tot);
+  int before = wave_excl(__popc(live), &tot);
+  uint32_t sel = above;
 #pragma unroll
   for (int i = 0; i < kP; ++i) {
-    if ((eq >> i) & 1u) {
+    if ((live >> i) & 1u) {
       if (before < remaining) sel |= 1u << i;
       ++before;
     }
