@@ -305,20 +305,40 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
 }
 
 // out[b][g] = merge over splits; one workgroup per (sequence, query head).
+// Splits are read eight at a time (all loads of a batch issued before any is
+// used), then merged in split order.
 template <int D>
 __global__ __launch_bounds__(D) void combine_kernel(AttnArgs a) {
+  constexpr int kB = 8;
   const int bg = blockIdx.x;
   const int d = threadIdx.x;
-  const size_t p0 = (size_t)bg * a.n_split;
+  const int n = a.n_split;
+  const size_t p0 = (size_t)bg * n;
   float mm = -INFINITY;
-  for (int s = 0; s < a.n_split; ++s) mm = fmaxf(mm, a.part_ml[2 * (p0 + s)]);
+  for (int s0 = 0; s0 < n; s0 += kB) {
+    float ms[kB];
+#pragma unroll
+    for (int u = 0; u < kB; ++u) ms[u] = s0 + u < n ? a.part_ml[2 * (p0 + s0 + u)] : -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kB; ++u) mm = fmaxf(mm, ms[u]);
+  }
   float num = 0.0f, den = 0.0f;
-  for (int s = 0; s < a.n_split; ++s) {
-    const float ms = a.part_ml[2 * (p0 + s)];
-    if (ms == -INFINITY) continue;
-    const float w = __builtin_amdgcn_exp2f(ms - mm);
-    den = fmaf(a.part_ml[2 * (p0 + s) + 1], w, den);
-    num = fmaf(a.part_o[(p0 + s) * D + d], w, num);
+  for (int s0 = 0; s0 < n; s0 += kB) {
+    float ms[kB], ls[kB], os[kB];
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+      const bool ok = s0 + u < n;
+      ms[u] = ok ? a.part_ml[2 * (p0 + s0 + u)] : -INFINITY;
+      ls[u] = ok ? a.part_ml[2 * (p0 + s0 + u) + 1] : 0.0f;
+      os[u] = ok ? a.part_o[(p0 + s0 + u) * D + d] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+      if (ms[u] == -INFINITY) continue;
+      const float w = __builtin_amdgcn_exp2f(ms[u] - mm);
+      den = fmaf(ls[u], w, den);
+      num = fmaf(os[u], w, num);
+    }
   }
   a.out[(size_t)bg * D + d] = num / den;
 }

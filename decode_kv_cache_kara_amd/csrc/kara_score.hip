@@ -19,8 +19,16 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ p
        i += (size_t)gridDim.x * blockDim.x) {
     const size_t u = i / C, j = i - (i / C) * C;
     const float* p = partials + u * n_split * C + j;
+    // chunks read eight at a time (loads issued before any add), added in order
     float s = 0.0f;
-    for (int k = 0; k < n_split; ++k) s += p[(size_t)k * C];
+    for (int k0 = 0; k0 < n_split; k0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = k0 + k < n_split ? p[(size_t)(k0 + k) * C] : 0.0f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (k0 + k < n_split) s += v[k];
+    }
     scores[i] = s;
   }
 }
