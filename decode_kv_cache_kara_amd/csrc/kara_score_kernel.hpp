@@ -380,8 +380,8 @@ __global__ __launch_bounds__(ScoreCfg<T>::kThreads, ScoreCfg<T>::kMinWavesPerEU)
     };
     // Two ways to accumulate the row statistics.  Exact: a running maximum,
     // updated every subtile, with the sum rescaled when it moves.  Fixed
-    // reference (the method's scoring, not the unidirectional ablation): the
-    // maximum of the lane's first 16 keys is the reference for the whole row, so
+    // reference (the first run of pass 1): the maximum of the lane's first 16
+    // visible keys is the reference for the whole row, so
     // every subtile costs one multiply-add, one exp2 and one add per logit.  The
     // sum is then exact in the same way (it is scaled by a power of two fixed
     // per row) unless a later logit exceeds the reference by more than the
@@ -494,13 +494,12 @@ __global__ __launch_bounds__(ScoreCfg<T>::kThreads, ScoreCfg<T>::kMinWavesPerEU)
     // The first two key tiles of pass 2 are fetched now, to arrive while
     // pass 1 is checked and the row biases are published; they are stored once
     // every wave is past pass 1 (its LDS tiles are then free).
+    // The unidirectional ablation takes the same fixed reference: a causal
+    // row whose lane half sees none of its first keys (window positions 0-3)
+    // makes the workgroup rerun pass 1 exactly, which happens only in a
+    // unit's first chunk.
     Stage p2_t0, p2_t1;
-    if constexpr (kUni) {
-      pass1(std::true_type());
-      load_tile(p2_t0, 0);
-      load_tile(p2_t1, (T2 > 1 ? 1 : 0) * kKeyTile);
-      __syncthreads();
-    } else {
+    {
       pass1(std::false_type());
       load_tile(p2_t0, 0);
       load_tile(p2_t1, (T2 > 1 ? 1 : 0) * kKeyTile);
