@@ -143,7 +143,7 @@ __global__ __launch_bounds__(ScoreCfg<T>::kThreads, ScoreCfg<T>::kMinWavesPerEU)
   constexpr int kWaves = ScoreCfg<T>::kWaves;
   constexpr int kThreads = ScoreCfg<T>::kThreads;
   constexpr int kKeyTile = ScoreCfg<T>::kKeyTile;
-  constexpr int kChunksPerWG = ScoreCfg<T>::kChunksPerWG;
+  constexpr int kChunksPerWG = kUni ? 1 : ScoreCfg<T>::kChunksPerWG;
   constexpr int kSub = kKeyTile / 32;               // 32-key subtiles per tile
   using M = Mma<T>;
   typedef typename M::Frag Frag;
@@ -623,7 +623,8 @@ __global__ __launch_bounds__(ScoreCfg<T>::kThreads, ScoreCfg<T>::kMinWavesPerEU)
 template <typename T, int D>
 hipError_t launch_score_typed(const ScoreArgs& a, hipStream_t stream) {
   const int units_pad = (a.n_units + 7) / 8 * 8;
-  const unsigned groups = (unsigned)((a.n_split + ScoreCfg<T>::kChunksPerWG - 1) / ScoreCfg<T>::kChunksPerWG);
+  const int per_wg = a.unidirectional ? 1 : ScoreCfg<T>::kChunksPerWG;
+  const unsigned groups = (unsigned)((a.n_split + per_wg - 1) / per_wg);
   const unsigned grid = (unsigned)units_pad * groups;
   if (a.unidirectional)
     hipLaunchKernelGGL((score_kernel<T, D, true>), dim3(grid), dim3(ScoreCfg<T>::kThreads), 0, stream, a);
