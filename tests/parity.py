@@ -17,6 +17,78 @@ from oracle import kara_oracle as ko
 
 SCORE_RTOL = 1e-3       # tolerance on the window scores (float32 accumulate vs float64)
 
+# Per-case parity counts, printed at the end of the session (tests/conftest.py)
+# and written as JSON where KARA_PARITY_REPORT names a file.
+TALLY: dict = {}
+
+
+def tally(case, verdicts=None, max_rel_err=None, replayed=0):
+    """Adds one check's results to the session's per-case counts."""
+    t = TALLY.setdefault(case, {"exact": 0, "near_tie": 0, "fail": 0, "replayed_bit_exact": 0,
+                                "max_score_rel_err": 0.0})
+    for v, n in (verdicts or {}).items():
+        key = "fail" if v.startswith("fail") else v
+        t[key] = t.get(key, 0) + n
+    if max_rel_err is not None:
+        t["max_score_rel_err"] = max(t["max_score_rel_err"], float(max_rel_err))
+    t["replayed_bit_exact"] += int(replayed)
+    return t
+
+
+def _replay_chunk(args):
+    """Worker: the oracle's Top-K and Token2Chunk on the GPU's own float32
+    scores of a run of units; returns the units whose results differ."""
+    gs, cand, kept, K, R, chunks, first = args
+    bad = []
+    for i in range(gs.shape[0]):
+        if (cand[i].tolist() != ko.topk_candidates(gs[i], K).tolist()
+                or kept[i].tolist() != ko.select_retained(gs[i], K, R, chunks=chunks).tolist()):
+            bad.append(first + i)
+    return bad
+
+
+_POOL = None
+
+
+def cpu_workers():
+    """CPU worker processes for large replays (spawned: they import NumPy and
+    the oracle only and never touch the GPU)."""
+    global _POOL
+    if _POOL is None:
+        import concurrent.futures
+        import multiprocessing
+        import os
+        n = max(1, min(8, len(os.sched_getaffinity(0)) - 1))
+        _POOL = concurrent.futures.ProcessPoolExecutor(max_workers=n,
+                                                       mp_context=multiprocessing.get_context("spawn"))
+    return _POOL
+
+
+def replay_mismatches(gpu_scores, cand, kept, K, R, chunks=True):
+    """Units whose candidates or kept set differ from the oracle's Top-K and
+    Token2Chunk run in float32 on the GPU's own float32 scores."""
+    gs = np.ascontiguousarray(np.asarray(gpu_scores, dtype=np.float32))
+    cand = np.asarray(cand)
+    kept = np.asarray(kept)
+    U = gs.shape[0]
+    if U * gs.shape[1] <= 2_000_000:
+        return _replay_chunk((gs, cand, kept, K, R, chunks, 0))
+    step = max(64, U // 64)
+    jobs = [(gs[a:a + step], cand[a:a + step], kept[a:a + step], K, R, chunks, a) for a in range(0, U, step)]
+    return [u for part in cpu_workers().map(_replay_chunk, jobs) for u in part]
+
+
+def replay_selection(gpu_scores, cand, kept, K, R, chunks=True):
+    """Selection parity on the GPU's own scores: for every unit, the oracle's
+    Top-K and Token2Chunk, run in float32 on the float32 scores the GPU
+    produced, give exactly the GPU's candidates and kept set.  All decisions
+    of these stages are comparisons and correctly rounded float32 operations,
+    so nothing is left to tolerance.  Returns the number of units checked."""
+    U = np.asarray(gpu_scores).shape[0]
+    bad = replay_mismatches(gpu_scores, cand, kept, K, R, chunks)
+    assert not bad, f"replay differs from the GPU on {len(bad)} of {U} units, first {bad[:8]}"
+    return U
+
 
 def host_inputs(wl):
     """Oracle-side copies of a workload's inputs: float64 states, int tables."""
@@ -55,7 +127,7 @@ def _close(a, b, tol):
     return abs(a - b) <= tol * max(abs(a), abs(b))
 
 
-def adjudicate(s, K, R, X, candX, tol=2 * SCORE_RTOL, chunks=True):
+def adjudicate(s, K, R, X, candX, tol=SCORE_RTOL, chunks=True):
     """Classify the GPU's kept set X and candidates candX of one unit against the
     oracle's float64 scores s: 'exact', 'near_tie' or 'fail: reason'.
     chunks=False judges the Token2Chunk-off ablation (X must be a top-R set).
@@ -146,3 +218,28 @@ def bits(t):
     if t.dtype == torch.float32:
         return t.view(torch.int32)
     return t
+
+
+def _scores_job(args):
+    q, k, protect, uni = args
+    return ko.window_scores(q, k, protect, unidirectional=uni)
+
+
+def oracle_scores_many(pairs, protect, unidirectional=False):
+    """The oracle's float64 window scores for a list of (q_window, k_window)
+    host arrays, computed in the CPU worker processes."""
+    jobs = [(q, k, protect, unidirectional) for q, k in pairs]
+    if len(jobs) <= 2:
+        return [_scores_job(j) for j in jobs]
+    return list(cpu_workers().map(_scores_job, jobs))
+
+
+def pair_verdicts_job(args):
+    """Worker: float64 oracle scores of one (sequence, layer) pair, their
+    largest relative difference from the GPU's scores, and the verdicts of the
+    GPU's kept sets against them (one per KV head)."""
+    q, k, protect, top_k, budget, gpu_scores, cand, kept = args
+    s = ko.window_scores(q, k, protect)
+    err = float((np.abs(gpu_scores - s) / np.abs(s)).max())
+    verdicts = [adjudicate(s[h], top_k, budget, kept[h], cand[h]) for h in range(s.shape[0])]
+    return err, verdicts

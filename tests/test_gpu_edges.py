@@ -66,7 +66,7 @@ def test_edge_end_to_end(name):
     wl = synth.make_workload(None, device="cuda", **EDGE_CASES[name])
     orc = oracle_scores(wl)
     ses, pool, before = run_e2e(wl)
-    verdicts = check_e2e(wl, ses, pool, before, orc)
+    verdicts = check_e2e(wl, ses, pool, before, orc, case=f"edge {name}")
     say(name, verdicts)
 
 

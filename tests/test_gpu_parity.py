@@ -15,7 +15,7 @@ import torch
 
 from oracle import kara_oracle as ko
 from parity import (SCORE_RTOL, adjudicate, assert_scores_close, bits, expected_rows, host_inputs,
-                    oracle_scores, tail_rows)
+                    oracle_scores, replay_selection, tail_rows, tally)
 
 pytestmark = pytest.mark.gpu
 
@@ -202,11 +202,14 @@ def run_e2e(wl):
     return ses, pool, before
 
 
-def check_e2e(wl, ses, pool, before, orc_scores):
+def check_e2e(wl, ses, pool, before, orc_scores, case=None):
     U, C = wl.n_units, wl.region
-    assert_scores_close(ses.scores.cpu().numpy(), orc_scores.reshape(U, C))
+    gs = ses.scores.cpu().numpy()
+    worst = assert_scores_close(gs, orc_scores.reshape(U, C))
     cand = ses.cand.cpu().numpy()
     kept = ses.retained.cpu().numpy()
+    # the selection stages replayed on the GPU's own float32 scores: bit for bit
+    replayed = replay_selection(gs, cand, kept, wl.top_k, wl.budget)
     verdicts = {}
     for u in range(U):
         v = adjudicate(orc_scores.reshape(U, C)[u], wl.top_k, wl.budget, kept[u], cand[u])
@@ -239,6 +242,8 @@ def check_e2e(wl, ses, pool, before, orc_scores):
     fresh = {int(x) for row in new_table for x in row if x >= 0} - {int(x) for x in table.ravel() if x >= 0}
     keep = [i for i in range(wl.n_blocks) if i not in fresh]
     assert torch.equal(after[:, :, keep], old[:, :, keep])
+    if case:
+        tally(case, verdicts, worst, replayed)
     return verdicts
 
 
@@ -250,7 +255,7 @@ def test_compress_end_to_end(name):
     wl = gpu_workload(cfg, **p)
     orc = oracle_scores(wl)
     ses, pool, before = run_e2e(wl)
-    verdicts = check_e2e(wl, ses, pool, before, orc)
+    verdicts = check_e2e(wl, ses, pool, before, orc, case=f"e2e {name}")
     say(name, verdicts)
     if name in ("tiny-fp32", "sharp-logits-bf16"):
         assert verdicts.get("exact", 0) == wl.n_units   # well-separated scores: no ties to adjudicate

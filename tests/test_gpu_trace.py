@@ -1,16 +1,26 @@
-"""GPU test of the periodic-compression serving trace (Distill-Llama-8B shapes,
-reduced: 16 sequences x 2 layers, 24 events).  At every event that compresses
-something, the call is checked against the oracle on the exact bytes it read:
-scores within 1e-3, kept sets exact or adjudicated near-ties, the compacted
-rows byte-exact against the old cache, tables/lengths/free list against the
-oracle's pool model, and the schedule against the oracle's."""
+"""GPU tests of the periodic-compression serving trace (Distill-Llama-8B
+shapes).
+
+Reduced trace (16 sequences x 2 layers, 24 events): at every event that
+compresses something, the call is checked against the oracle on the exact
+bytes it read: scores within 1e-3, the selection replayed on the GPU's own
+float32 scores bit for bit, kept sets exact or adjudicated near-ties against
+float64 scores, the compacted rows byte-exact against the old cache,
+tables/lengths/free list against the oracle's pool model, and the schedule
+against the oracle's.
+
+Full trace (128 sequences x 32 layers, 240 events): every event's schedule and
+bookkeeping against the oracle, the selection of every unit of every event
+replayed bit for bit, and one sampled (sequence, layer) pair per event (8
+units) scored by the float64 oracle with its compacted rows checked byte for
+byte."""
 
 import numpy as np
 import pytest
 import torch
 
 from oracle import kara_oracle as ko
-from parity import adjudicate, assert_scores_close
+from parity import cpu_workers, adjudicate, assert_scores_close, pair_verdicts_job, replay_selection, tally
 
 pytestmark = pytest.mark.gpu
 
@@ -26,6 +36,8 @@ def test_serving_trace_small():
     c = cfg
     U_per_seq = c.n_layers * c.n_kv_heads
     checked = 0
+    replayed = 0
+    worst = 0.0
     verdicts = {}
     while not tr.done():
         lens_before = tr.phys.copy()
@@ -57,7 +69,10 @@ def test_serving_trace_small():
         # scores and selections of every unit in the batch
         qn = q.cpu().double().numpy()
         pn = pool_before.double().numpy()
-        S_ = outs["scores"].cpu().numpy().reshape(nb, c.n_layers, c.n_kv_heads, -1)
+        gs = outs["scores"].cpu().numpy()
+        replayed += replay_selection(gs, outs["cand"].cpu().numpy(), outs["retained"].cpu().numpy(),
+                                     c.top_k, c.budget)
+        S_ = gs.reshape(nb, c.n_layers, c.n_kv_heads, -1)
         cand = outs["cand"].cpu().numpy().reshape(nb, c.n_layers, c.n_kv_heads, -1)
         kept = outs["retained"].cpu().numpy().reshape(nb, c.n_layers, c.n_kv_heads, -1)
         for i in range(nb):
@@ -65,7 +80,7 @@ def test_serving_trace_small():
             for l in range(c.n_layers):
                 kw = ko.window_keys(pn, table_h[i].numpy(), L, c.window, l, c.n_kv_heads, c.block_size)
                 s = ko.window_scores(qn[i, l], kw, c.protect)
-                assert_scores_close(S_[i, l], s)
+                worst = max(worst, assert_scores_close(S_[i, l], s))
                 for h in range(c.n_kv_heads):
                     v = adjudicate(s[h], c.top_k, c.budget, kept[i, l, h], cand[i, l, h])
                     assert not v.startswith("fail"), (tr.events, i, l, h, v)
@@ -91,7 +106,98 @@ def test_serving_trace_small():
                         assert torch.equal(src, dst)
         checked += 1
     print("[case] events", tr.events, "checked", checked, verdicts, flush=True)
+    tally("serving trace 16x2x24", verdicts, worst, replayed)
     assert checked >= 3
     # lengths follow the host replay of the schedule
     n_events, _, _ = simulate_schedule(cfg)
     assert tr.events == n_events
+
+
+@pytest.mark.timeout(1200)
+def test_serving_trace_full():
+    """The whole Distill-Llama-8B-shaped trace: 128 sequences x 32 layers,
+    lengths 2048 -> 32768, 240 events of period 128 with half the sequences
+    offered at each event."""
+    print("[case] serving trace full", flush=True)
+    cfg = TraceConfig()
+    tr = ServingTrace(cfg)
+    c = cfg
+    bs = c.block_size
+    rng = np.random.default_rng(4)
+    jobs = []
+    replayed = 0
+    n_events = 0
+    while not tr.done():
+        batch = tr.next_event()
+        sel = tr.last_selected
+        assert batch == ko.schedule_step(tr.step, c.period, c.window, tr.phys.tolist(),
+                                         tr.watermark.tolist(), sel.tolist())
+        if not batch:
+            continue
+        q = tr.window_queries(batch)
+        nb = len(batch)
+        table_h, _, lens_h, _ = tr.batch_inputs(batch)
+        # one sampled (sequence, layer) pair: its window keys and old tail rows before compression
+        i, l = int(rng.integers(nb)), int(rng.integers(c.n_layers))
+        L = int(lens_h[i])
+        start = L - c.window
+        f0 = start // bs
+        toks = torch.arange(f0 * bs, L, dtype=torch.long)
+        blk = table_h[i].long()[toks // bs].cuda()
+        off = (toks % bs).cuda()
+        tail = [tr.pool[l, kv, blk, :, off, :].cpu() for kv in range(2)]     # [n, Hkv, D]
+        k_win = tail[0][start - f0 * bs:].float().numpy()
+        q_pair = q[i, l].float().cpu().numpy()
+        free_before = tr.blocks.snapshot()
+        U = nb * c.n_layers * c.n_kv_heads
+        outs = dict(scores=torch.empty((U, c.window - c.protect), device="cuda"),
+                    cand=torch.empty((U, c.top_k), dtype=torch.int32, device="cuda"),
+                    retained=torch.empty((U, c.budget), dtype=torch.int32, device="cuda"))
+        table_h, lens_h, new_table_h, new_lens_h = tr.compress(batch, q, outputs=outs)
+        torch.cuda.synchronize()
+        fifo = ko.FifoPool(free_before)
+        want_table, want_lens = ko.plan_compaction(table_h.numpy().astype(np.int64),
+                                                   lens_h.numpy().astype(np.int64), c.window,
+                                                   c.protect, c.budget, bs, fifo)
+        assert new_table_h.numpy().tolist() == want_table.tolist()
+        assert new_lens_h.numpy().tolist() == want_lens.tolist()
+        assert tr.blocks.snapshot() == fifo.ids()
+        gs = outs["scores"].cpu().numpy()
+        cand = outs["cand"].cpu().numpy()
+        kept = outs["retained"].cpu().numpy()
+        replayed += replay_selection(gs, cand, kept, c.top_k, c.budget)
+        # the sampled pair: compacted rows byte for byte, scores and kept sets later (CPU workers)
+        u0 = (i * c.n_layers + l) * c.n_kv_heads
+        n_new = (start - f0 * bs) + c.budget + c.protect
+        ntoks = torch.arange(f0 * bs, f0 * bs + n_new, dtype=torch.long)
+        nblk = new_table_h[i].long()[ntoks // bs].cuda()
+        noff = (ntoks % bs).cuda()
+        p = start - f0 * bs
+        for kv in range(2):
+            got = tr.pool[l, kv, nblk, :, noff, :].cpu().view(torch.int16)
+            old = tail[kv].view(torch.int16)
+            for h in range(c.n_kv_heads):
+                idx = list(range(p)) + [p + int(j) for j in kept[u0 + h]] + list(range(p + c.window - c.protect,
+                                                                                      p + c.window))
+                assert torch.equal(old[idx, h], got[:, h]), (tr.events, i, l, h, kv)
+        jobs.append((tr.events, i, l, cpu_workers().submit(
+            pair_verdicts_job, (q_pair, k_win, c.protect, c.top_k, c.budget, gs[u0:u0 + c.n_kv_heads],
+                        cand[u0:u0 + c.n_kv_heads], kept[u0:u0 + c.n_kv_heads]))))
+        n_events += 1
+        if n_events % 40 == 0:
+            print(f"[case] trace event {tr.events}: {n_events} compressions checked, {replayed} units replayed",
+                  flush=True)
+    verdicts = {}
+    worst = 0.0
+    for ev, i, l, fut in jobs:
+        err, vs = fut.result()
+        assert err <= 1e-3, (ev, i, l, err)
+        worst = max(worst, err)
+        for h, v in enumerate(vs):
+            assert not v.startswith("fail"), (ev, i, l, h, v)
+            verdicts[v] = verdicts.get(v, 0) + 1
+    tally("serving trace 128x32x240", verdicts, worst, replayed)
+    print(f"[case] full trace: {tr.events} events, {n_events} compressions, {replayed} units replayed, "
+          f"{verdicts}, max score rel err {worst:.3g}", flush=True)
+    assert tr.events == simulate_schedule(cfg)[0]
+    assert n_events >= 200
