@@ -12,10 +12,18 @@ resident in HBM.  Prints one JSON line:
              stream around that kernel inside the timed steps
   cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
                 on all host threads (cpu_baseline_1core: one thread, smaller sample)
+  parity     every unit's selection replayed by the oracle on the GPU's own
+             float32 scores, and the sampled units of cpu_baseline against the
+             float64 oracle (exact / near-tie accepted / failed)
   measured_ceilings  the chip's own MFMA, VALU, interleaved and copy rates from
                 the library's probes, and the kernels' times against them
+  secondary  the Qwen3-4B-shaped batch (32 sequences x 36 layers, W=1024),
+             timed after the main workload
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+The default workload is the largest single-GPU one: Qwen3-14B-shaped, 128
+sequences x 40 layers, W=2048 (config 3).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3]
 """
 
 from __future__ import annotations
@@ -59,37 +67,104 @@ def read_traffic(workload):
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(cfg, n_layers_sample, seed, n_seqs_sample=3, flags=0, one_core=False):
-    """Oracle compress() on n_seqs_sample sequences x n_layers_sample layers of
-    the same shapes, extrapolated to the metric's unit (window tokens of the
-    full model slice per second)."""
+def host_cores():
+    """Cores this process may run on (its CPU affinity)."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def sample_workload(wl, seqs, layers):
+    """Host float64 copies of the inputs of the sampled (sequence, layer)
+    pairs as a self-contained small workload: window queries [n_s, n_l, W, Hq,
+    D], a pool [n_l, 2, NB', Hkv, bs, D] holding only the blocks from each
+    sampled sequence's boundary block to its end (ids renumbered), the
+    renumbered tables and the lengths."""
     import numpy as np
     import torch
-    from threadpoolctl import threadpool_info
 
-    from decode_kv_cache_kara_amd import synth
+    bs, W = wl.block_size, wl.window
+    lens = [int(x) for x in wl.lens.cpu().tolist()]
+    table = wl.table.cpu().long()
+    li = torch.tensor(layers, dtype=torch.long, device=wl.pool.device)
+    ids, rows = [], []
+    MB = 0
+    for b in seqs:
+        f0, f1 = (lens[b] - W) // bs, -(-lens[b] // bs)
+        row = np.full(f1, -2, dtype=np.int64)
+        for e in range(f0, f1):
+            row[e] = len(ids)
+            ids.append(int(table[b, e]))
+        rows.append(row)
+        MB = max(MB, f1)
+    tab = np.full((len(seqs), MB), -1, dtype=np.int64)
+    for i, row in enumerate(rows):
+        tab[i, :len(row)] = row
+    blk = torch.tensor(ids, dtype=torch.long, device=wl.pool.device)
+    pool = wl.pool.index_select(0, li).index_select(2, blk).to("cpu", torch.float64).numpy()
+    q = torch.stack([wl.q_window[b].index_select(0, li) for b in seqs]).to("cpu", torch.float64).numpy()
+    return q, pool, tab, np.array([lens[b] for b in seqs], dtype=np.int64)
+
+
+def cpu_baseline(wl, seqs, layers, flags=0, one_core=False, gpu=None):
+    """The oracle's compress() (float64 scores, Top-K, Token2Chunk) timed on
+    the sampled (sequence, layer) pairs of the benchmark's own workload,
+    scaled to the metric's unit (window tokens of the whole model slice per
+    second: a pair is 1 / n_layers of one sequence's window).  With the GPU's
+    outputs for the same workload (`gpu`: host scores, candidates and kept
+    sets of every unit), the sampled units' parity against this oracle run is
+    counted: exact, near-tie accepted (tests/parity.py's rule at 1e-3) or
+    failed, and the largest relative score difference."""
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+
     from oracle import kara_oracle as ko
 
-    full = synth.CONFIGS[cfg]
-    wl = synth.make_workload(cfg, seed=seed, device="cpu", n_seqs=n_seqs_sample, n_layers=n_layers_sample)
-    q = wl.q_window.to(torch.float64).numpy()
-    pool = wl.pool.to(torch.float64).numpy()
-    table = wl.table.long().numpy()
-    lens = wl.lens.long().numpy()
-    from threadpoolctl import threadpool_limits
-
+    uni, chunks = bool(flags & 1), not (flags & 2)
+    q, pool, tab, lens = sample_workload(wl, seqs, layers)
+    units = [(i, j) for i in range(len(seqs)) for j in range(len(layers))]
     with threadpool_limits(limits=1 if one_core else None):
         t0 = time.perf_counter()
-        ko.compress(q, pool, table, lens, wl.window, wl.protect, wl.top_k, wl.budget, wl.block_size,
-                    wl.free_ids, unidirectional=bool(flags & 1), chunks=not (flags & 2))
+        res = ko.compress(q, pool, tab, lens, wl.window, wl.protect, wl.top_k, wl.budget, wl.block_size, [],
+                          units=units, unidirectional=uni, chunks=chunks)
         dt = time.perf_counter() - t0
-    frac = n_layers_sample / full["n_layers"]
-    value = n_seqs_sample * wl.window * frac / dt
-    threads = 1 if one_core else max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    return {"value": value, "unit": "window tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": (f"oracle compress() (fp64 scores, Top-K, Token2Chunk, pool plan, row gather) on "
-                       f"{n_seqs_sample} sequences x {n_layers_sample} of {full['n_layers']} layers of the same "
-                       f"shapes (L={[int(x) for x in lens]}), {dt:.1f} s, scaled to the full layer count")}
+    value = len(units) / wl.n_layers * wl.window / dt
+    blas = 1 if one_core else max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    out = {"value": value, "unit": "window tokens/s", "cores": int(blas), "host_cores": host_cores(),
+           "kind": "oracle",
+           "sample": (f"oracle compress() (float64 scores, Top-K, Token2Chunk) on {len(units)} (sequence, layer) "
+                      f"pairs = {len(units) * wl.n_kv_heads} units of this workload (sequences {list(seqs)}, "
+                      f"layers {list(layers)} of {wl.n_layers}), {dt:.1f} s with {blas} BLAS thread(s), scaled to "
+                      f"window tokens of the whole {wl.n_layers}-layer slice")}
+    if gpu is not None:
+        sys.path.insert(0, os.path.join(ROOT, "tests"))
+        from parity import adjudicate
+        Hkv = wl.n_kv_heads
+        counts = {"exact": 0, "near_tie": 0, "fail": 0}
+        worst = 0.0
+        for i, b in enumerate(seqs):
+            for j, l in enumerate(layers):
+                for h in range(Hkv):
+                    u = (b * wl.n_layers + l) * Hkv + h
+                    s = res["scores"][i, j, h]
+                    worst = max(worst, float((np.abs(gpu["scores"][u] - s) / np.abs(s)).max()))
+                    v = adjudicate(s, wl.top_k, wl.budget, gpu["kept"][u], gpu["cand"][u], chunks=chunks)
+                    counts["fail" if v.startswith("fail") else v] += 1
+        out["parity"] = dict(counts, units=len(units) * Hkv, max_score_rel_err=worst)
+    return out
+
+
+def replay_parity(wl, gpu, flags=0):
+    """Every unit's selection replayed by the oracle in float32 on the GPU's
+    own float32 scores (CPU worker processes); counts the units that differ
+    (the bar is zero)."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from parity import replay_mismatches
+    t0 = time.perf_counter()
+    bad = replay_mismatches(gpu["scores"], gpu["cand"], gpu["kept"], wl.top_k, wl.budget, chunks=not (flags & 2))
+    return {"units": int(gpu["scores"].shape[0]), "mismatches": len(bad), "first": bad[:8],
+            "seconds": round(time.perf_counter() - t0, 1)}
 
 
 def measured_ceilings(score_ms, exec_flop, exec_logits, compact_ms, compact_bytes):
@@ -280,18 +355,149 @@ def run_trace(args, out_base):
     return out
 
 
+def run_batch(cfg, args, flags, steps, warmup, extras=True, keep_outputs=False):
+    """Times `steps` kara_compress calls on one synthetic workload (inputs
+    resident in HBM; `warmup` untimed calls first) and returns the report
+    fields, the workload and, with keep_outputs, host copies of one further
+    call's scores, candidates and kept sets."""
+    import torch
+
+    from decode_kv_cache_kara_amd import kara, runner, synth
+
+    t0 = time.time()
+    wl = synth.make_workload(cfg, seed=args.seed, device="cuda")
+    torch.cuda.synchronize()
+    log(f"workload {wl.name}: {wl.n_seqs} seqs x {wl.n_layers} layers, pool {wl.n_blocks} blocks "
+        f"({wl.pool.numel() * wl.pool.element_size() / 2**30:.1f} GiB), generated in {time.time() - t0:.1f} s")
+    ses = runner.Session(wl, outputs=False, flags=flags)
+    stream = torch.cuda.current_stream()
+
+    def events():
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        for e in ev:
+            e.record(stream)      # materialise the handles
+        return ev
+
+    for _ in range(warmup):
+        ses.compress(stream=stream)
+    torch.cuda.synchronize()
+    log(f"warmup done ({warmup} steps)")
+
+    step_events = [events() for _ in range(steps)]
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for k in range(steps):
+        ses.compress(stream=stream, stage_events=[e.cuda_event for e in step_events[k]])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / steps
+    stage = [0.0, 0.0, 0.0]
+    for ev in step_events:
+        for i in range(3):
+            stage[i] += ev[i].elapsed_time(ev[i + 1])
+    stage = [x / steps for x in stage]
+    per_step = sorted(ev[0].elapsed_time(ev[3]) for ev in step_events)
+    log(f"timed {steps} steps: {ms_per_step:.3f} ms/step; score {stage[0]:.3f} ms, "
+        f"select {stage[1]:.3f} ms, compact {stage[2]:.3f} ms")
+
+    S, Lyr, Hq, Hkv, D, W, C = (wl.n_seqs, wl.n_layers, wl.n_q_heads, wl.n_kv_heads, wl.head_dim,
+                                wl.window, wl.region)
+    elt = wl.pool.element_size()
+    tokens = S * W
+    value = tokens / (ms_per_step / 1e3)
+    uni = bool(flags & kara.UNIDIRECTIONAL)
+    # one QK^T over the window: all W x W logits, or (unidirectional) the
+    # W (W + 1) / 2 that causal attention needs
+    score_flop = 2.0 * S * Lyr * Hq * (W * (W + 1) / 2 if uni else W * W) * D
+    exec_flop = 2.0 * S * Lyr * Hq * W * (math.ceil(W / 64) * 64 + math.ceil(C / 64) * 64) * D
+    score_tflops = score_flop / (stage[0] / 1e3) / 1e12
+    peak = PEAK_BF16_TFLOPS if wl.dtype == torch.bfloat16 else PEAK_FP32_MFMA_TFLOPS
+    lens = ses.lens_h.tolist()
+    rows = sum(((L - W) % wl.block_size) + wl.budget + wl.protect for L in lens)
+    compact_bytes = 2.0 * rows * Lyr * 2 * Hkv * D * elt
+    compact_gbs = compact_bytes / (stage[2] / 1e3) / 1e9
+    traffic = read_traffic(wl.name) if flags == 0 else None
+    materialized = not bool((wl.table == -2).any())
+
+    out = {
+        "value": round(value, 1),
+        "ms_per_step": round(ms_per_step, 4),
+        "dtype": "bf16" if wl.dtype == torch.bfloat16 else "f32",
+        "config": {"workload": wl.name, "n_seqs": S, "n_layers": Lyr, "n_q_heads": Hq, "n_kv_heads": Hkv,
+                   "head_dim": D, "window": W, "protect": wl.protect, "top_k": wl.top_k,
+                   "budget": wl.budget, "block_size": wl.block_size,
+                   "seq_lens": f"U[{min(lens)}..{max(lens)}] seed {wl.seed}",
+                   "prefix_blocks": "materialised" if materialized else
+                   "not materialised (table entries before the boundary block are never read by the step)",
+                   "ablation": {0: "none", 1: "unidirectional", 2: "no_chunks", 3: "unidirectional+no_chunks"}[flags]},
+        "roofline": {"bound": "mfma", "kernel": "score_kernel", "achieved": round(score_tflops, 2),
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(score_tflops / peak, 4),
+                     "traffic": traffic, "algorithmic_flop_per_launch": score_flop,
+                     "executed_mfma_flop_per_launch": exec_flop if not uni else None},
+        "stages_ms": {"score": round(stage[0], 4), "select": round(stage[1], 4),
+                      "compact": round(stage[2], 4)},
+        "kernel_ms_per_step": {"median": round(per_step[len(per_step) // 2], 4), "min": round(per_step[0], 4),
+                               "max": round(per_step[-1], 4)},
+        "compact_roofline": {"bound": "hbm", "kernel": "compact_kernel", "achieved": round(compact_gbs, 1),
+                             "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(compact_gbs / PEAK_HBM_GBS, 4),
+                             "algorithmic_bytes_per_launch": compact_bytes},
+    }
+    if extras and materialized:
+        out["decode_attention"] = decode_attention_roofline(ses, wl)
+        log(f"decode attention over the compacted cache: {out['decode_attention']['ms_per_launch']:.3f} ms/layer, "
+            f"{out['decode_attention']['achieved']:.0f} GB/s")
+    elif extras:
+        out["decode_attention"] = {"skipped": "the workload's prefix blocks are not materialised, so attention "
+                                              "over whole sequences would re-read one block; measured on the "
+                                              "Qwen3-4B-shaped batch instead"}
+    if extras and wl.dtype == torch.bfloat16 and not uni:
+        exec_logits = exec_flop / (2.0 * D)
+        out["measured_ceilings"] = measured_ceilings(stage[0], exec_flop, exec_logits, stage[2], compact_bytes)
+        mc = out["measured_ceilings"]
+        log(f"measured ceilings: MFMA {mc['mfma_bf16_tflops']} TFLOP/s, softmax VALU {mc['valu_softmax_gelem_per_s']} "
+            f"Gelem/s, interleaved {mc['mix_glogits_per_s']} Glogit/s, copy {mc['copy_gbs']} GB/s; score kernel at "
+            f"{mc['score_kernel']['frac_of_interleaved']:.1%} of its interleaved bound")
+    gpu = None
+    if keep_outputs:
+        outs = runner.Session(wl, outputs=True, flags=flags)
+        outs.compress(stream=stream)
+        torch.cuda.synchronize()
+        gpu = {"scores": outs.scores.cpu().numpy(), "cand": outs.cand.cpu().numpy(),
+               "kept": outs.retained.cpu().numpy()}
+        del outs
+    del ses
+    return out, wl, gpu
+
+
+def spread(n, k):
+    """k indices spread over range(n), the first and the last included."""
+    if k >= n:
+        return list(range(n))
+    return sorted({round(i * (n - 1) / (k - 1)) for i in range(k)})
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None,
                     help="timed steps (default 20; for the trace, all events after warmup)")
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=2, choices=[0, 1, 2, 3, 4])
+    ap.add_argument("--config", type=int, default=3, choices=[0, 1, 2, 3, 4],
+                    help="workload (default 3: Qwen3-14B-shaped, 128 sequences x 40 layers, W=2048)")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--flags", type=int, default=0, choices=[0, 1, 2, 3],
                     help="ablations: 1 unidirectional scoring, 2 Token2Chunk off, 3 both")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-layers", type=int, default=36)
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the Qwen3-4B-shaped batch measured after the main workload")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time the step only (no decode attention, probes or policy simulation)")
+    ap.add_argument("--cpu-pairs", type=str, default="4x8",
+                    help="oracle sample: sequences x layers of the workload (default 4x8 = 32 pairs)")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
                     help="only run a device-to-device copy of this many GiB three times (the reference "
                          "kernel that scales the HBM byte counters) and print its size")
@@ -307,8 +513,6 @@ def main():
 
     import torch
 
-    from decode_kv_cache_kara_amd import kara, runner, synth
-
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
@@ -323,126 +527,47 @@ def main():
         print(json.dumps({"copy_bytes_per_launch": n, "launches": 3}), flush=True)
         return
 
+    base = {"metric": METRIC, "unit": "window tokens/s", "n_gpus": 1, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16"}
     if args.config == 4:
-        base = {"metric": METRIC, "unit": "window tokens/s", "n_gpus": 1, "higher_is_better": True,
-                "scaling": "weak", "vs_baseline": None, "dtype": "bf16"}
         out = run_trace(args, base)
-        if not args.no_cpu_baseline:
-            log("timing the CPU oracle on a sample ...")
-            out["cpu_baseline"] = cpu_baseline(4, min(args.cpu_layers, 32), seed=7)
         print(json.dumps(out), flush=True)
         return
 
-    t0 = time.time()
-    wl = synth.make_workload(args.config, seed=args.seed, device="cuda")
-    torch.cuda.synchronize()
-    log(f"workload {wl.name}: {wl.n_seqs} seqs x {wl.n_layers} layers, pool {wl.n_blocks} blocks "
-        f"({wl.pool.numel() * wl.pool.element_size() / 2**30:.1f} GiB), generated in {time.time() - t0:.1f} s")
-    ses = runner.Session(wl, outputs=False, flags=args.flags)
-    stream = torch.cuda.current_stream()
-
-    def events():
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-        for e in ev:
-            e.record(stream)      # materialise the handles
-        return ev
-
-    for _ in range(args.warmup):
-        ses.compress(stream=stream)
-    torch.cuda.synchronize()
-    log(f"warmup done ({args.warmup} steps)")
-
-    step_events = [events() for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for k in range(args.steps):
-        ses.compress(stream=stream, stage_events=[e.cuda_event for e in step_events[k]])
-    stop.record(stream)
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
-    ms_per_step = total_ms / args.steps
-    stage = [0.0, 0.0, 0.0]
-    for ev in step_events:
-        for i in range(3):
-            stage[i] += ev[i].elapsed_time(ev[i + 1])
-    stage = [x / args.steps for x in stage]
-    per_step = sorted(ev[0].elapsed_time(ev[3]) for ev in step_events)
-    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step; score {stage[0]:.3f} ms, "
-        f"select {stage[1]:.3f} ms, compact {stage[2]:.3f} ms")
-
-    S, Lyr, Hq, Hkv, D, W, C = (wl.n_seqs, wl.n_layers, wl.n_q_heads, wl.n_kv_heads, wl.head_dim,
-                                wl.window, wl.region)
-    elt = wl.pool.element_size()
-    tokens = S * W
-    value = tokens / (ms_per_step / 1e3)
-    uni = bool(args.flags & kara.UNIDIRECTIONAL)
-    # one QK^T over the window: all W x W logits, or (unidirectional) the
-    # W (W + 1) / 2 that causal attention needs
-    score_flop = 2.0 * S * Lyr * Hq * (W * (W + 1) / 2 if uni else W * W) * D
-    exec_flop = 2.0 * S * Lyr * Hq * W * (math.ceil(W / 64) * 64 + math.ceil(C / 64) * 64) * D
-    score_tflops = score_flop / (stage[0] / 1e3) / 1e12
-    peak = PEAK_BF16_TFLOPS if wl.dtype == torch.bfloat16 else PEAK_FP32_MFMA_TFLOPS
-    lens = ses.lens_h.tolist()
-    rows = sum(((L - W) % wl.block_size) + wl.budget + wl.protect for L in lens)
-    compact_bytes = 2.0 * rows * Lyr * 2 * Hkv * D * elt
-    compact_gbs = compact_bytes / (stage[2] / 1e3) / 1e9
-    traffic = read_traffic(wl.name) if args.flags == 0 else None
-
-    out = {
-        "metric": METRIC,
-        "value": round(value, 1),
-        "unit": "window tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16" if wl.dtype == torch.bfloat16 else "f32",
-        "data": "synthetic (seeded Gaussian Q/K/V with planted spans; fragmented block tables)",
-        "config": {"workload": wl.name, "n_seqs": S, "n_layers": Lyr, "n_q_heads": Hq, "n_kv_heads": Hkv,
-                   "head_dim": D, "window": W, "protect": wl.protect, "top_k": wl.top_k,
-                   "budget": wl.budget, "block_size": wl.block_size,
-                   "seq_lens": f"U[{min(lens)}..{max(lens)}] seed {wl.seed}",
-                   "ablation": {0: "none", 1: "unidirectional", 2: "no_chunks", 3: "unidirectional+no_chunks"}[args.flags]},
-        "roofline": {"bound": "mfma", "kernel": "score_kernel", "achieved": round(score_tflops, 2),
-                     "peak": peak, "unit": "TFLOP/s", "frac": round(score_tflops / peak, 4),
-                     "traffic": traffic, "algorithmic_flop_per_launch": score_flop,
-                     "executed_mfma_flop_per_launch": exec_flop if not uni else None},
-        "stages_ms": {"score": round(stage[0], 4), "select": round(stage[1], 4),
-                      "compact": round(stage[2], 4)},
-        "kernel_ms_per_step": {"median": round(per_step[len(per_step) // 2], 4), "min": round(per_step[0], 4),
-                               "max": round(per_step[-1], 4)},
-        "compact_roofline": {"bound": "hbm", "kernel": "compact_kernel", "achieved": round(compact_gbs, 1),
-                             "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(compact_gbs / PEAK_HBM_GBS, 4),
-                             "algorithmic_bytes_per_launch": compact_bytes},
-    }
-    out["decode_attention"] = decode_attention_roofline(ses, wl)
-    log(f"decode attention over the compacted cache: {out['decode_attention']['ms_per_launch']:.3f} ms/layer, "
-        f"{out['decode_attention']['achieved']:.0f} GB/s")
-    if wl.dtype == torch.bfloat16 and not uni:
-        exec_logits = exec_flop / (2.0 * D)
-        out["measured_ceilings"] = measured_ceilings(stage[0], exec_flop, exec_logits, stage[2], compact_bytes)
-        mc = out["measured_ceilings"]
-        log(f"measured ceilings: MFMA {mc['mfma_bf16_tflops']} TFLOP/s, softmax VALU {mc['valu_softmax_gelem_per_s']} "
-            f"Gelem/s, interleaved {mc['mix_glogits_per_s']} Glogit/s, copy {mc['copy_gbs']} GB/s; score kernel at "
-            f"{mc['score_kernel']['frac_of_interleaved']:.1%} of its interleaved bound")
-    if args.flags == 0 and args.config == 2:       # costs scaled from the Qwen3-4B-shaped slice
-        out["policy_sim"] = policy_sim(out, wl)
+    res, wl, gpu = run_batch(args.config, args, args.flags, args.steps, args.warmup, extras=not args.no_extras,
+                             keep_outputs=not args.no_cpu_baseline)
+    out = dict(base)
+    out.update({"value": res.pop("value"), "steps": args.steps, "warmup": args.warmup,
+                "ms_per_step": res.pop("ms_per_step"), "dtype": res.pop("dtype"),
+                "data": "synthetic (seeded Gaussian Q/K/V; planted spans where the workload has them; fragmented "
+                        "block tables)",
+                "config": res.pop("config")})
+    out.update(res)
     if not args.no_cpu_baseline:
-        del ses, wl
-        torch.cuda.empty_cache()
-        log("timing the CPU oracle on a sample ...")
-        n_layers_sample = min(args.cpu_layers, synth.CONFIGS[args.config]["n_layers"])
-        out["cpu_baseline"] = cpu_baseline(args.config, n_layers_sample, seed=7, flags=args.flags)
-        log(f"cpu baseline {out['cpu_baseline']['value']:.1f} window tokens/s")
-        out["cpu_baseline_1core"] = cpu_baseline(args.config, min(8, n_layers_sample), seed=7, n_seqs_sample=1,
-                                                 flags=args.flags, one_core=True)
+        log("timing the CPU oracle on a sample of the same workload ...")
+        n_s, n_l = (int(x) for x in args.cpu_pairs.split("x"))
+        seqs, layers = spread(wl.n_seqs, n_s), spread(wl.n_layers, n_l)
+        out["cpu_baseline"] = cpu_baseline(wl, seqs, layers, flags=args.flags, gpu=gpu)
+        log(f"cpu baseline {out['cpu_baseline']['value']:.1f} window tokens/s; sampled parity "
+            f"{out['cpu_baseline']['parity']}")
+        out["cpu_baseline_1core"] = cpu_baseline(wl, seqs[:1], layers[:1], flags=args.flags, one_core=True)
         log(f"cpu baseline on one core {out['cpu_baseline_1core']['value']:.1f} window tokens/s")
+        out["parity"] = {"replay_all_units": replay_parity(wl, gpu, args.flags),
+                         "sampled_vs_float64_oracle": out["cpu_baseline"]["parity"],
+                         "rule": "scores within 1e-3 relative; selection replayed in float32 on the GPU's scores "
+                                 "bit-exact for every unit; sampled units exact or near-ties within 1e-3"}
+        log(f"replay of every unit: {out['parity']['replay_all_units']}")
+    if args.config == 2 and args.flags == 0 and not args.no_extras:
+        out["policy_sim"] = policy_sim(out, wl)
+    del wl, gpu
+    torch.cuda.empty_cache()
+    if args.config == 3 and not args.no_secondary:
+        sec, wl2, _ = run_batch(2, args, args.flags, max(10, args.steps // 2), args.warmup,
+                                extras=not args.no_extras)
+        out["secondary"] = sec
+        if args.flags == 0 and not args.no_extras:
+            out["policy_sim"] = policy_sim(sec, wl2)
+        del wl2
     print(json.dumps(out), flush=True)
 
 
