@@ -142,10 +142,39 @@ def test_pool_exhaustion_changes_nothing():
 
 
 def test_kv_bytes_of_the_pages():
+    """The pages' 20 GB for 128K Qwen3-14B tokens in FP16, through the oracle's
+    own cache layout: the bytes apply_compaction writes for one kept token of
+    one layer (its K and V rows of every KV head) times tokens times layers."""
     with open(os.path.join(GOLD, "kv_bytes.json")) as f:
         w = json.load(f)
-    per_token_per_layer = 2 * w["n_kv_heads"] * w["head_dim"] * w["elt_bytes"]   # K and V rows of all heads
+    Hkv, D, bs = w["n_kv_heads"], w["head_dim"], 16
+    W, B = 32, 4
+    L = W
+    table = np.array([[0, 1]])
+    pool = np.zeros((1, 2, 4, Hkv, bs, D), dtype=np.float16)
+    pool[:, :, :2] = 1.0                                   # old blocks 0, 1; fresh blocks 2, 3 are empty
+    new_table = np.array([[2, 3]])
+    R = W - B                                              # keep every token of the region
+    kept = np.arange(R).reshape(1, 1, 1, R).repeat(Hkv, axis=2)
+    out = ko.apply_compaction(pool, table, np.array([L]), new_table, W, B, R, bs, kept)
+    written = int((out[:, :, 2:] != pool[:, :, 2:]).sum()) * pool.itemsize
+    per_token_per_layer = written // (R + B)
+    assert per_token_per_layer == 2 * Hkv * D * w["elt_bytes"]
     assert w["tokens"] * w["n_layers"] * per_token_per_layer == w["bytes"] == 20 * 2 ** 30
+
+
+def test_schedule_worked_example_oracle():
+    """The oracle's schedule on a hand-worked step (period 128, W = 1024):
+    sequence 0 holds 3000 tokens past its watermark (eligible), sequence 1 only
+    500, sequence 2 is shorter than the window, sequence 3 was not selected;
+    off the period and at step 0 nothing is compressed."""
+    lens, wm, sel = [3000, 5000, 900, 2048], [0, 4500, 0, 0], [1, 1, 1, 0]
+    assert ko.schedule_step(256, 128, 1024, lens, wm, sel) == [0]
+    assert ko.schedule_step(128, 128, 1024, lens, wm, sel) == [0]
+    assert ko.schedule_step(200, 128, 1024, lens, wm, sel) == []
+    assert ko.schedule_step(0, 128, 1024, lens, wm, sel) == []
+    # exactly W tokens past the watermark is eligible, one fewer is not
+    assert ko.schedule_step(128, 128, 1024, [2024, 2023], [1000, 1000], [1, 1]) == [0]
 
 
 def test_end_to_end_tiny_consistent():
