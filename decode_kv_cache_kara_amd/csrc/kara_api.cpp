@@ -12,6 +12,7 @@
 #include <cstdio>
 #include <cstring>
 #include <deque>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -710,6 +711,78 @@ kara_status kara_probe(int32_t kind, int64_t iters, void* dst_d, const void* src
   }
   hipError_t e = kara::launch_probe(kind, iters, dst_d, src_d, n_bytes, n_cu, (hipStream_t)stream, work_out);
   return e == hipSuccess ? KARA_OK : hip_fail(e, "probe launch");
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// kara_compress_static: kara_compress for callers that cannot allocate device
+// memory.  Its scratch (the scoring kernel's partial column sums and the kept
+// positions) lives in one file-scope device array per GPU, loaded with the
+// library's code object; host code reaches it only through the address
+// hipGetSymbolAddress returns for the current device.
+
+static __device__ __align__(256) char scratch[KARA_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The array's device address on the current device, looked up on the first
+// call on that device (with the device current) and kept.
+kara_status static_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(KARA_E_UNSUPPORTED, "device %d beyond %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "static scratch address");
+    if (!ptr) return fail(KARA_E_HIP, "static scratch address is NULL");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return KARA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kara_static_scratch_bytes(void) { return (size_t)KARA_STATIC_SCRATCH_BYTES; }
+
+kara_status kara_compress_static(const kara_shape* shape, const kara_params* params, int32_t n_seqs,
+                                 const void* q_window, void* kv_pool, int32_t n_blocks,
+                                 const int32_t* block_table_h, const int32_t* block_table_d,
+                                 int32_t max_blocks, const int32_t* seq_lens_h, const int32_t* seq_lens_d,
+                                 kara_pool* pool, int32_t* new_block_table_h, int32_t* new_block_table_d,
+                                 int32_t* new_seq_lens_h, void* stream, float* scores_out_d,
+                                 int32_t* cand_out_d, int32_t* retained_out_d, void* const* stage_events) {
+  kara_status st;
+  if ((st = check_shape(shape)) != KARA_OK) return st;
+  if ((st = check_params(params)) != KARA_OK) return st;
+  if (n_seqs < 0) return fail(KARA_E_INVAL, "n_seqs < 0");
+  const size_t need = layout(shape, params, n_seqs).total;
+  if (need > (size_t)KARA_STATIC_SCRATCH_BYTES)
+    return fail(KARA_E_WORKSPACE,
+                "kara_compress_static: %d sequences need %zu bytes of scratch, the static scratch holds %zu; "
+                "compress fewer sequences per call or use kara_compress with a workspace",
+                n_seqs, need, (size_t)KARA_STATIC_SCRATCH_BYTES);
+  if (n_seqs == 0)
+    return compress_impl(shape, params, 0, QuerySource{q_window, nullptr}, kv_pool, n_blocks, block_table_h,
+                         block_table_d, max_blocks, seq_lens_h, seq_lens_d, pool, new_block_table_h,
+                         new_block_table_d, new_seq_lens_h, nullptr, 0, stream, scores_out_d, cand_out_d,
+                         retained_out_d, stage_events);
+  void* ptr = nullptr;
+  if ((st = static_scratch(&ptr)) != KARA_OK) return st;
+  return compress_impl(shape, params, n_seqs, QuerySource{q_window, nullptr}, kv_pool, n_blocks, block_table_h,
+                       block_table_d, max_blocks, seq_lens_h, seq_lens_d, pool, new_block_table_h,
+                       new_block_table_d, new_seq_lens_h, ptr, (size_t)KARA_STATIC_SCRATCH_BYTES, stream,
+                       scores_out_d, cand_out_d, retained_out_d, stage_events);
 }
 
 }  // extern "C"

@@ -109,6 +109,9 @@ _SIGS = {
     "kara_decode_attention": (_I, [_P, _I, _I, _P, _P, _I, _P, _I, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "kara_sim_gen_length": (_I, [_P, _I]),
     "kara_policy_sim": (_I, [_P, _P, _P, _P, _P]),
+    "kara_static_scratch_bytes": (ctypes.c_size_t, []),
+    "kara_compress_static": (_I, [_P, _P, _I, _P, _P, _I, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                  _P]),
     "kara_probe_scratch_bytes": (ctypes.c_size_t, []),
     "kara_probe": (_I, [_I, ctypes.c_int64, _P, _P, ctypes.c_size_t, _P, ctypes.POINTER(ctypes.c_double)]),
 }
@@ -249,6 +252,29 @@ def kara_compress(shape, params, q_window, kv_pool, block_table_h, block_table_d
         workspace.numel() * workspace.element_size() if workspace is not None else 0,
         _stream(stream), _dev(scores_out, "scores_out", torch.float32),
         _dev(cand_out, "cand_out", torch.int32), _dev(retained_out, "retained_out", torch.int32), ev))
+
+
+def kara_static_scratch_bytes():
+    return int(_lib.kara_static_scratch_bytes())
+
+
+def kara_compress_static(shape, params, q_window, kv_pool, block_table_h, block_table_d, seq_lens_h,
+                         seq_lens_d, pool, new_block_table_h, new_block_table_d, new_seq_lens_h,
+                         stream=None, scores_out=None, cand_out=None, retained_out=None, stage_events=None):
+    """kara_compress without a workspace argument: the library's static scratch
+    serves instead (no device allocation; see include/kara.h)."""
+    n_seqs = seq_lens_h.numel()
+    ev = (_P * 4)(*stage_events) if stage_events is not None else None
+    _check(_lib.kara_compress_static(
+        ctypes.byref(shape), ctypes.byref(params), n_seqs, _dev(q_window, "q_window"),
+        _dev(kv_pool, "kv_pool"), kv_pool.shape[2], _host_i32(block_table_h, "block_table_h"),
+        _dev(block_table_d, "block_table_d", torch.int32), block_table_h.shape[1],
+        _host_i32(seq_lens_h, "seq_lens_h"), _dev(seq_lens_d, "seq_lens_d", torch.int32),
+        pool.handle, _host_i32(new_block_table_h, "new_block_table_h"),
+        _dev(new_block_table_d, "new_block_table_d", torch.int32),
+        _host_i32(new_seq_lens_h, "new_seq_lens_h"), _stream(stream),
+        _dev(scores_out, "scores_out", torch.float32), _dev(cand_out, "cand_out", torch.int32),
+        _dev(retained_out, "retained_out", torch.int32), ev))
 
 
 def kara_score(shape, params, q_window, kv_pool, block_table_h, block_table_d, seq_lens_h,

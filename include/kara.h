@@ -242,6 +242,33 @@ kara_status kara_paged_compact(const kara_shape* shape, const kara_params* param
                                int32_t* new_block_table_h, int32_t* new_block_table_d,
                                int32_t* new_seq_lens_h, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the whole
+ * step exactly as kara_compress, with the same arguments minus the
+ * workspace, and the same kernels and results.  Its scratch (the partial
+ * column sums and the kept positions, kara_workspace_bytes() bytes) is a
+ * device array of KARA_STATIC_SCRATCH_BYTES (256 MiB) inside the library,
+ * one per GPU, held until the process ends; its address is looked up on the
+ * first call on each device (make that call outside graph capture).  The call
+ * allocates no device memory.  Calls whose scratch need exceeds the array
+ * fail with KARA_E_WORKSPACE and change nothing (at W=1024, C=896 the array
+ * holds about 9,000 units of (sequence, layer, KV head); at W=2048, C=1792
+ * about 1,800).  Every call on one GPU shares that GPU's array: calls that
+ * overlap in time on one GPU (other host threads, other streams) race and
+ * must be serialised by the caller; nothing in it needs clearing between
+ * calls (every byte a call reads was written earlier in the same call). */
+#define KARA_STATIC_SCRATCH_BYTES ((size_t)256 << 20)
+size_t kara_static_scratch_bytes(void);
+kara_status kara_compress_static(const kara_shape* shape, const kara_params* params, int32_t n_seqs,
+                                 const void* q_window, void* kv_pool, int32_t n_blocks,
+                                 const int32_t* block_table_h, const int32_t* block_table_d,
+                                 int32_t max_blocks, const int32_t* seq_lens_h,
+                                 const int32_t* seq_lens_d, kara_pool* pool,
+                                 int32_t* new_block_table_h, int32_t* new_block_table_d,
+                                 int32_t* new_seq_lens_h, void* stream, float* scores_out_d,
+                                 int32_t* cand_out_d, int32_t* retained_out_d,
+                                 void* const* stage_events);
+
 /* ------------------------------------------------------------------------
  * Around the step: keeping the window's query states, and decode attention
  * over the (compressed) paged cache.

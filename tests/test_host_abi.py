@@ -216,3 +216,21 @@ def test_schedule_rejects():
         kara.kara_schedule_step(128, 128, 10, lens, torch.tensor([101], dtype=torch.int32), torch.tensor([1]))
     with pytest.raises(kara.KaraError):
         kara.kara_schedule_step(128, 0, 10, lens, torch.tensor([0], dtype=torch.int32), torch.tensor([1]))
+
+
+def test_compress_static_rejects_oversized_batch_before_side_effects():
+    """The no-allocation entry point refuses a batch whose scratch need exceeds
+    its static array, before reading any argument beyond shape and params."""
+    sh, pr = shape(), params()
+    assert kara.kara_static_scratch_bytes() == 256 << 20
+    n = 1
+    while kara.kara_workspace_bytes(sh, pr, n) <= kara.kara_static_scratch_bytes():
+        n *= 2
+    assert kara.kara_workspace_bytes(sh, pr, n) > kara.kara_static_scratch_bytes()
+    pool = kara.Pool(20, list(range(20)))
+    st = kara.lib.kara_compress_static(
+        ctypes.byref(sh), ctypes.byref(pr), n, FAKE * 16, FAKE * 16, 20, FAKE, FAKE * 16, 5, FAKE, FAKE * 16,
+        pool.handle, FAKE, FAKE * 16, FAKE, None, None, None, None, None)
+    assert st == kara.KARA_E_WORKSPACE
+    assert "static scratch" in kara.kara_last_error()
+    assert pool.snapshot() == list(range(20))
