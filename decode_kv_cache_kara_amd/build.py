@@ -13,7 +13,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkara.so")
 SOURCES = ["kara_api.cpp", "kara_score.hip", "kara_score_bf16_d128.hip", "kara_score_bf16_d64.hip",
-           "kara_score_f32_d128.hip", "kara_score_f32_d64.hip", "kara_select.hip", "kara_compact.hip",
+           "kara_score_f32_d128.hip", "kara_score_f32_d64.hip", "kara_score_resident.hip", "kara_select.hip", "kara_compact.hip",
            "kara_decode.hip", "kara_policy.cpp", "kara_probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

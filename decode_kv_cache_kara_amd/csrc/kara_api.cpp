@@ -179,7 +179,8 @@ Workspace layout(const kara_shape* sh, const kara_params* p, int32_t n_seqs) {
   const size_t U = (size_t)n_seqs * sh->n_layers * sh->n_kv_heads;
   const int C = p->window - p->protect;
   const int G = sh->n_q_heads / sh->n_kv_heads;
-  const size_t n_split = (size_t)kara::score_chunks(G, p->window);
+  const size_t n_split = (size_t)kara::score_splits(sh->dtype, sh->head_dim, p->window, G,
+                                                   (p->flags & KARA_UNIDIRECTIONAL) ? 1 : 0);
   Workspace w;
   w.partials = 0;
   w.retained = align_up(U * n_split * C * sizeof(float));
@@ -208,7 +209,7 @@ kara::ScoreArgs score_args(const kara_shape* sh, const kara_params* p, int32_t n
   a.MB = max_blocks;
   a.W = p->window;
   a.C = p->window - p->protect;
-  a.n_split = kara::score_chunks(a.G, a.W);
+  a.n_split = kara::score_splits(sh->dtype, a.D, a.W, a.G, (p->flags & KARA_UNIDIRECTIONAL) ? 1 : 0);
   a.n_units = n_seqs * sh->n_layers * sh->n_kv_heads;
   a.c = (float)(1.4426950408889634 / std::sqrt((double)sh->head_dim));
   a.unidirectional = (p->flags & KARA_UNIDIRECTIONAL) ? 1 : 0;

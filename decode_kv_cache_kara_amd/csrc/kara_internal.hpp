@@ -36,7 +36,24 @@ inline int score_chunks(int G, int W) {
   return (G * W + kScoreRowsPerChunk - 1) / kScoreRowsPerChunk;
 }
 
+// One-pass scoring with the window's keys resident in registers
+// (kara_score_resident.hip): bf16 states, head size 128, windows of at most
+// 1024 keys, at most 16384 rows per unit, the method's bidirectional scoring.
+// It writes each unit's scores directly (one "chunk" per unit).
+constexpr int kResidentMaxWindow = 1024;
+constexpr int kResidentMaxRows = 16384;
+
+inline bool use_resident(int dtype, int D, int W, int G, int unidirectional) {
+  return dtype == 1 && D == 128 && W <= kResidentMaxWindow && G * W <= kResidentMaxRows && !unidirectional;
+}
+
+// Partial column-sum rows per unit that the scorer writes.
+inline int score_splits(int dtype, int D, int W, int G, int unidirectional) {
+  return use_resident(dtype, D, W, G, unidirectional) ? 1 : score_chunks(G, W);
+}
+
 hipError_t launch_score(const ScoreArgs& a, int dtype, hipStream_t stream);
+hipError_t launch_score_resident(const ScoreArgs& a, hipStream_t stream);
 
 // Sums the n_split partial rows of every unit (in chunk order) into scores.
 hipError_t launch_reduce(const float* partials, float* scores, int n_units, int n_split, int C,

@@ -37,6 +37,10 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ p
 
 hipError_t launch_score(const ScoreArgs& a, int dtype, hipStream_t stream) {
   if (a.n_units == 0) return hipSuccess;
+  if (use_resident(dtype, a.D, a.W, a.G, a.unidirectional)) {
+    if (a.n_split != 1) return hipErrorInvalidValue;
+    return launch_score_resident(a, stream);
+  }
   if (dtype == 1) {
     if (a.D == 128) return launch_score_typed<__bf16, 128>(a, stream);
     if (a.D == 64) return launch_score_typed<__bf16, 64>(a, stream);

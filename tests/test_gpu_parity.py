@@ -52,6 +52,19 @@ SCORE_CASES = {
     "sharp-logits-bf16": dict(n_seqs=2, n_layers=2, n_q_heads=16, n_kv_heads=4, head_dim=128,
                               block_size=16, window=300, protect=40, top_k=16, budget=60,
                               lens=(300, 900), dtype=torch.bfloat16, qk_std=0.6),
+    # windows of up to 1024 keys held in registers: a ragged last wave (W = 1000,
+    # region not a multiple of 16), the largest row count (G = 16), a tiny
+    # window (two 16-key tiles per wave, most keys past the window), no
+    # protected buffer
+    "resident-w1000-g5": dict(n_seqs=2, n_layers=1, n_q_heads=10, n_kv_heads=2, head_dim=128, block_size=16,
+                              window=1000, protect=123, top_k=40, budget=175, lens=(1000, 3000),
+                              dtype=torch.bfloat16, qk_std=0.3),
+    "resident-w1024-g16": dict(n_seqs=1, n_layers=1, n_q_heads=32, n_kv_heads=2, head_dim=128, block_size=16,
+                               window=1024, protect=128, top_k=64, budget=179, lens=[5000],
+                               dtype=torch.bfloat16, qk_std=0.2),
+    "resident-w17-b0": dict(n_seqs=3, n_layers=2, n_q_heads=6, n_kv_heads=3, head_dim=128, block_size=8,
+                            window=17, protect=0, top_k=3, budget=9, lens=(17, 90), dtype=torch.bfloat16,
+                            qk_std=0.5),
 }
 
 
@@ -99,6 +112,34 @@ def test_score_stage_exact_fallback():
     orc = oracle_scores(wl).reshape(wl.n_units, wl.region)
     assert_scores_close(out.cpu().numpy(), orc)
     assert orc[0, j] > 0.9                     # the planted key took that row's whole weight
+
+
+def test_score_stage_exact_rerun_for_very_negative_logits():
+    """One query row whose logits with every window key are about -60 nats:
+    without a reference its normaliser falls below float's comfortable range,
+    so the scorer must take the exact route (every row's maximum as its
+    reference).  The scores still match the oracle."""
+    say("score stage exact rerun, very negative logits")
+    wl = gpu_workload(None, n_seqs=1, n_layers=1, n_q_heads=4, n_kv_heads=1, head_dim=128, block_size=16,
+                      window=256, protect=32, top_k=8, budget=40, lens=[600], dtype=torch.bfloat16,
+                      qk_std=0.1)
+    L = int(wl.lens[0])
+    toks = torch.arange(L - wl.window, L)
+    blk = wl.table[0].long()[toks // wl.block_size]
+    off = toks % wl.block_size
+    u = torch.ones(128, device="cuda") / math.sqrt(128)
+    k = wl.pool[0, 0, blk, 0, off].float() + 2.0 * u           # every window key shares direction u
+    wl.pool[0, 0, blk, 0, off] = k.to(torch.bfloat16)
+    q = -(60.0 * math.sqrt(128) / 2.0) * u                       # logits about -60 nats with every key
+    wl.q_window[0, 0, 77, 1] = q.to(torch.bfloat16)
+    kq = wl.pool[0, 0, blk, 0, off].float() @ wl.q_window[0, 0, 77, 1].float() / math.sqrt(128)
+    assert float(kq.max()) < -50.0
+    ses = runner.Session(wl)
+    out = torch.full((wl.n_units, wl.region), float("nan"), device="cuda")
+    ses.score(out)
+    torch.cuda.synchronize()
+    orc = oracle_scores(wl).reshape(wl.n_units, wl.region)
+    assert_scores_close(out.cpu().numpy(), orc)
 
 
 REGIONS = [1, 7, 56, 187, 896, 1792, 2048]
@@ -191,6 +232,7 @@ E2E_CASES = {
     "budget-below-k": dict(n_seqs=2, n_layers=1, n_q_heads=4, n_kv_heads=2, head_dim=128, block_size=16,
                            window=96, protect=16, top_k=20, budget=7, lens=(96, 200), dtype=torch.bfloat16,
                            qk_std=0.5),
+    "resident-w1000-g5": SCORE_CASES["resident-w1000-g5"],
 }
 
 
