@@ -170,22 +170,36 @@ void commit_plan(kara_pool* pool, const Plan& plan) {
   }
 }
 
-// Workspace: [partial column sums of every 512-row chunk][retained positions]
+// Workspace: [partial column sums of every 512-row chunk (one row per unit
+// for the resident-key scorer)][resident scorer over two key blocks: per-row
+// normaliser inputs, per-unit exact-route flags][retained positions]
 struct Workspace {
-  size_t partials, retained, total;
+  size_t partials, zrow, flags, retained, total;
 };
 
 Workspace layout(const kara_shape* sh, const kara_params* p, int32_t n_seqs) {
   const size_t U = (size_t)n_seqs * sh->n_layers * sh->n_kv_heads;
   const int C = p->window - p->protect;
   const int G = sh->n_q_heads / sh->n_kv_heads;
-  const size_t n_split = (size_t)kara::score_splits(sh->dtype, sh->head_dim, p->window, G,
-                                                   (p->flags & KARA_UNIDIRECTIONAL) ? 1 : 0);
+  const int uni = (p->flags & KARA_UNIDIRECTIONAL) ? 1 : 0;
+  const size_t n_split = (size_t)kara::score_splits(sh->dtype, sh->head_dim, p->window, G, uni);
+  const bool two = kara::resident_two_blocks(sh->dtype, sh->head_dim, p->window, G, uni);
   Workspace w;
   w.partials = 0;
-  w.retained = align_up(U * n_split * C * sizeof(float));
+  w.zrow = align_up(U * n_split * C * sizeof(float));
+  w.flags = w.zrow + (two ? align_up(U * (size_t)G * p->window * sizeof(float)) : 0);
+  w.retained = w.flags + (two ? align_up(U * sizeof(int32_t)) : 0);
   w.total = w.retained + align_up(U * p->budget * sizeof(int32_t));
   return w;
+}
+
+// Points the scorer's per-row and per-unit buffers into the workspace.
+void attach_resident(kara::ScoreArgs* a, const kara_shape* sh, const kara_params* p, const Workspace& w,
+                     void* workspace) {
+  if (kara::resident_two_blocks(sh->dtype, sh->head_dim, p->window, a->G, a->unidirectional)) {
+    a->zrow = (float*)((char*)workspace + w.zrow);
+    a->uflags = (int32_t*)((char*)workspace + w.flags);
+  }
 }
 
 kara::ScoreArgs score_args(const kara_shape* sh, const kara_params* p, int32_t n_seqs,
@@ -216,6 +230,10 @@ kara::ScoreArgs score_args(const kara_shape* sh, const kara_params* p, int32_t n
   a.q_slots = nullptr;
   a.q_counts = nullptr;
   a.q_n_slots = 0;
+  a.zrow = nullptr;
+  a.uflags = nullptr;
+  a.key_lo = 0;
+  a.key_hi = 0;
   return a;
 }
 
@@ -377,6 +395,7 @@ kara_status compress_impl(const kara_shape* shape, const kara_params* params, in
   if ((e = mark(0)) != hipSuccess) return hip_fail(e, "stage event");
   kara::ScoreArgs sa = score_args(shape, params, n_seqs, q_window, kv_pool, n_blocks, block_table_d,
                                   max_blocks, seq_lens_d, partials);
+  attach_resident(&sa, shape, params, ws, workspace);
   if (qs.ring) {
     sa.q_slots = qs.ring->slots_d;
     sa.q_counts = qs.ring->counts_d;
@@ -566,13 +585,16 @@ kara_status kara_score(const kara_shape* shape, const kara_params* params, int32
     return fail(KARA_E_INVAL, "q_window and kv_pool must be 16-byte aligned");
   const Workspace ws = layout(shape, params, n_seqs);
   const int G = shape->n_q_heads / shape->n_kv_heads;
-  const bool direct = kara::score_chunks(G, params->window) == 1;
-  if (!direct && (!workspace || workspace_bytes < ws.retained || !is_aligned(workspace, kAlign)))
+  const int uni = (params->flags & KARA_UNIDIRECTIONAL) ? 1 : 0;
+  const bool direct = kara::score_splits(shape->dtype, shape->head_dim, params->window, G, uni) == 1;
+  if ((!direct || kara::resident_two_blocks(shape->dtype, shape->head_dim, params->window, G, uni)) &&
+      (!workspace || workspace_bytes < ws.retained || !is_aligned(workspace, kAlign)))
     return fail(KARA_E_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned", ws.retained);
   hipStream_t s = (hipStream_t)stream;
   float* partials = direct ? scores_d : (float*)((char*)workspace + ws.partials);
   kara::ScoreArgs sa = score_args(shape, params, n_seqs, q_window, kv_pool, n_blocks, block_table_d,
                                   max_blocks, seq_lens_d, partials);
+  attach_resident(&sa, shape, params, ws, workspace);
   hipError_t e = kara::launch_score(sa, shape->dtype, s);
   if (e != hipSuccess) return hip_fail(e, "score launch");
   if (!direct && (e = kara::launch_reduce(partials, scores_d, sa.n_units, sa.n_split, sa.C, s)) != hipSuccess)

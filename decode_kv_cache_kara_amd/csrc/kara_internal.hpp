@@ -30,22 +30,37 @@ struct ScoreArgs {
   const int32_t* q_slots; // null: q is [S][Lyr][W][Hq][D]
   const int32_t* q_counts;
   int q_n_slots;
+  // Resident-key scoring of windows longer than one key block: per-row
+  // normaliser inputs [U][G*W] and per-unit exact-route flags [U] (workspace).
+  float* zrow;
+  int32_t* uflags;
+  int key_lo, key_hi;     // resident key range of one launch (set by the launcher)
 };
 
 inline int score_chunks(int G, int W) {
   return (G * W + kScoreRowsPerChunk - 1) / kScoreRowsPerChunk;
 }
 
-// One-pass scoring with the window's keys resident in registers
+// Scoring with the window's keys resident in registers
 // (kara_score_resident.hip): bf16 states, head size 128, windows of at most
-// 1024 keys, at most 16384 rows per unit, the method's bidirectional scoring.
+// 2048 keys (one pass up to 1024 keys, three launches over two key blocks
+// beyond), at most 16384 rows per unit, the method's bidirectional scoring.
 // It writes each unit's scores directly (one "chunk" per unit).
-constexpr int kResidentMaxWindow = 1024;
+constexpr int kResidentBlock = 1024;
+constexpr int kResidentMaxWindow = 2 * kResidentBlock;
 constexpr int kResidentMaxRows = 16384;
 
 inline bool use_resident(int dtype, int D, int W, int G, int unidirectional) {
   return dtype == 1 && D == 128 && W <= kResidentMaxWindow && G * W <= kResidentMaxRows && !unidirectional;
 }
+
+// Whether the resident scorer needs the per-row and per-unit workspace.
+inline bool resident_two_blocks(int dtype, int D, int W, int G, int unidirectional) {
+  return use_resident(dtype, D, W, G, unidirectional) && W > kResidentBlock;
+}
+
+// N-tiles of 16 keys per wave (2, 4, 6 or 8) that hold n_keys keys.
+int resident_tiles(int n_keys);
 
 // Partial column-sum rows per unit that the scorer writes.
 inline int score_splits(int dtype, int D, int W, int G, int unidirectional) {

@@ -1,36 +1,50 @@
-// Window scoring in one pass over the logits, with the window's keys held in
-// registers ("Technical Summary: Kara", Methodology 1, Mechanism and
-// Rationale: every window query's softmax over all W window keys, with no
-// mask, is accumulated into the scores of the keys j < C = W - B).
+// Window scoring with the window's keys resident in registers ("Technical
+// Summary: Kara", Methodology 1, Mechanism and Rationale: every window query's
+// softmax over all W window keys, with no mask, is accumulated into the
+// scores of the keys j < C = W - B).
 //
 // The score of key j is  s[j] = sum_rows exp(x[row, j]) / Z[row]  with
 // Z[row] = sum over all W keys of exp(x[row, k]).  A row's normaliser is known
 // only after all of its keys, so a kernel that streams keys past resident
 // query rows must either compute every logit twice (once for Z, once for the
 // column sums) or keep every exponential until Z is known.  Here the roles are
-// swapped: one workgroup holds all (up to 1024) keys of a unit's window in
-// registers, 128 keys per wave of eight, and streams the unit's G*W query rows
-// past them in tiles of 16 rows.  Per tile each wave computes the 16 x 128
-// logits on the matrix cores (v_mfma_f32_16x16x32_bf16, the keys as the
-// resident B operand, the query rows as the A operand read from LDS), turns
-// them into exponentials in place, and adds its partial row sums into LDS;
-// after one workgroup barrier every wave reads the tile's 16 normalisers and
-// adds  exp * (1 / Z)  into per-key column accumulators.  Each logit costs one
-// multiply, one exp2, one add and (for keys of the compressible region) one
-// multiply-add, and its MFMA is issued once.
+// swapped: one workgroup holds up to 1024 keys of a unit's window in
+// registers, 16 NT keys per wave of eight, and streams the unit's G*W query
+// rows past them in tiles of 16 rows.  Per tile each wave computes the
+// 16 x 16 NT logits on the matrix cores (v_mfma_f32_16x16x32_bf16, the keys as
+// the resident B operand, the query rows as the A operand read from LDS),
+// turns them into exponentials in place, and publishes its partial row sums
+// in LDS; after one workgroup barrier every wave reads the tile's 16
+// normalisers and adds  exp * (1 / Z)  into per-key column accumulators.
+//
+// Windows of up to 1024 keys take one pass (mode kWhole): every logit's MFMA
+// and exp2 are issued once.  Longer windows (up to 2048 keys) take three
+// launches over two key blocks, KB0 = [0, 1024) and KB1 = [1024, W):
+//   kRowSums      KB1 resident: each row's partial normaliser over KB1;
+//   kWithRowSums  KB0 resident: the partial normaliser over KB0 plus the one
+//                 from KB1 gives Z; column sums of KB0's region keys; 1 / Z
+//                 stored per row;
+//   kWeighted     KB1 resident again: column sums of KB1's region keys
+//                 [1024, C) with the stored 1 / Z.
+// Only KB1's region keys are computed twice: 1024 + 1024 + (C - 1024) logits
+// per row (2816 at W = 2048, C = 1792) instead of W + C = 3840 for a kernel
+// that recomputes the whole region.
 //
 // The exponentials take no per-row reference (exp2 of the logit in log2
 // units).  That is exact in the same sense as a row-maximum reference as long
 // as no sum leaves float's range; a row whose normaliser lies outside
-// [2^-40, 2^100] (logits beyond about +-27 / 69 nats) sends the workgroup to an
-// exact rerun of the unit that first takes every row's maximum and then uses
-// it as the reference (slow, never taken on ordinary data).
+// [2^-40, 2^100] (logits beyond about +-27 / 69 nats) sends the unit to an
+// exact route that first takes every row's maximum over all keys, then the
+// normalisers with those references, then the column sums (slow, key block by
+// key block; never taken on ordinary data).  For two-block windows the check
+// is made by kWithRowSums and the exact route run by kWeighted.
 //
-// Registers (two waves per SIMD, at most 256 each): 128 for the keys, 64 for
-// two logit tiles (the next tile's MFMAs run while the VALU works on the
-// current one), 16 for the query fragments, 8 column accumulators.  LDS: a
-// ring of four 16-row query tiles (rows padded to 272 bytes), the per-wave row
-// sums, and (exact rerun only) one reference per row.
+// Registers (two waves per SIMD, at most 256 each): 4 NT x 4 for the keys,
+// 2 x 4 NT for two logit tiles (the next tile's MFMAs run while the VALU works
+// on the current one), 16 for the query fragments, NT column accumulators.
+// LDS: a ring of four 16-row query tiles (rows padded to 272 bytes), the
+// per-wave row sums, staged per-row normaliser inputs, and (exact route) one
+// reference and one normaliser per row.
 
 #include "kara_internal.hpp"
 
@@ -48,15 +62,16 @@ constexpr int kRRows = 16;                     // query rows per tile
 constexpr int kRKs = 4;                        // 32-wide reduction steps over D = 128
 constexpr int kRQStride = 272;                 // LDS bytes per staged query row (256 + pad)
 constexpr int kRQSlots = 4;                    // query tiles in the LDS ring
-constexpr int kRMaxRefRows = kResidentMaxRows; // rows with an LDS reference in the exact rerun
+
+enum Mode { kWhole = 0, kRowSums = 1, kWithRowSums = 2, kWeighted = 3 };
 
 template <int kCtrl>
 __device__ __forceinline__ float dpp(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, 0xF, 0xF,
-                                                               false));
+  const int xi = __builtin_bit_cast(int, x);
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(xi, xi, kCtrl, 0xF, 0xF, true));
 }
 
-// Sum over the 16 lanes of a DPP row (rotations by 8, 4, 2, 1 reach every lane).
+// Sum / maximum over the 16 lanes of a DPP row (rotations by 8, 4, 2, 1).
 __device__ __forceinline__ float row_sum16(float x) {
   x += dpp<0x128>(x);   // row_ror:8
   x += dpp<0x124>(x);   // row_ror:4
@@ -73,16 +88,28 @@ __device__ __forceinline__ float row_max16(float x) {
   return x;
 }
 
+// Row sums of a tile over the 16 lanes (keys) of a DPP row, transposed: the
+// lane starts with its partial sums of rows 0..3 of its row group and ends with
+// the full sum of row (lane & 15) >> 2.  Lanes i and 15 - i (row_mirror) and
+// then i and 7 - i (row_half_mirror) swap the halves they do not keep; the
+// last two steps sum within the quad.
+__device__ __forceinline__ float row_sums16_transposed(const float (&rp)[4], int kl) {
+  const bool hi8 = kl & 8, hi4 = kl & 4;
+  const float k0 = hi8 ? rp[2] : rp[0], s0 = hi8 ? rp[0] : rp[2];
+  const float k1 = hi8 ? rp[3] : rp[1], s1 = hi8 ? rp[1] : rp[3];
+  const float a0 = k0 + dpp<0x140>(s0);   // row_mirror
+  const float a1 = k1 + dpp<0x140>(s1);
+  const float kk = hi4 ? a1 : a0, ss = hi4 ? a0 : a1;
+  float v = kk + dpp<0x141>(ss);          // row_half_mirror
+  v += dpp<0xB1>(v);                      // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);                      // quad_perm [2,3,0,1]
+  return v;
+}
+
 // Sum over the 4 lanes of a quad.
 __device__ __forceinline__ float quad_sum(float x) {
   x += dpp<0xB1>(x);    // quad_perm [1,0,3,2]
   x += dpp<0x4E>(x);    // quad_perm [2,3,0,1]
-  return x;
-}
-
-__device__ __forceinline__ float quad_max(float x) {
-  x = fmaxf(x, dpp<0xB1>(x));
-  x = fmaxf(x, dpp<0x4E>(x));
   return x;
 }
 
@@ -96,11 +123,18 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-template <int NT>
+template <int NT, int MODE>
 __global__ __launch_bounds__(kRThreads, 2) void score_resident_kernel(ScoreArgs a) {
+  constexpr bool kRowSumsHere = MODE != kWeighted;     // this launch computes row normalisers
+  constexpr bool kCols = MODE != kRowSums;              // this launch adds column sums
+  constexpr bool kStageRow = MODE == kWithRowSums || MODE == kWeighted;   // a per-row input is staged
+  constexpr int kBlockKeys = kRWaves * 16 * NT;
+
   __shared__ __attribute__((aligned(16))) char qbuf[kRQSlots][kRRows * kRQStride];
   __shared__ __attribute__((aligned(16))) float zpart[2][kRWaves][kRRows];
-  __shared__ float refs[kRMaxRefRows];
+  __shared__ __attribute__((aligned(16))) float rowin[kRQSlots][kRRows];
+  __shared__ float refs[kResidentMaxRows];
+  __shared__ float zfull[kResidentMaxRows];
   __shared__ int s_redo;
 
   const int unit = blockIdx.x;
@@ -139,59 +173,91 @@ __global__ __launch_bounds__(kRThreads, 2) void score_resident_kernel(ScoreArgs 
   const char* kbase = (const char*)a.pool + ((size_t)l * 2 * a.NB * a.Hkv * a.bs + (size_t)h * a.bs) * 256;
   const size_t blk_bytes = (size_t)a.Hkv * a.bs * 256;
   const int bs_mask = (1 << a.bs_shift) - 1;
+  float* zrow = a.zrow ? a.zrow + (size_t)unit * rows : nullptr;
+  float* out = a.out + (size_t)unit * C;
 
-  // ---- the wave's keys: B operand fragments, resident for the whole unit ----
-  // Key of N-tile nt for this lane: k0 + 16 nt + kl; the lane holds its
-  // 16-byte pieces (lane >> 4) + 4 ks, ks = 0..3, of that key's 256-byte row.
-  const int k0 = wave * 16 * NT;
+  // ---- resident keys: B operand fragments ----
+  // Key of N-tile nt for this lane: lo + 16 NT wave + 16 nt + kl; the lane
+  // holds its 16-byte pieces (lane >> 4) + 4 ks, ks = 0..3, of that key's
+  // 256-byte row.  Keys at or past `hi` are zero (logit 0).
   bf16x8 kf[NT][kRKs];
-  float n_inval = 0.0f;                 // this lane's keys past the window (their logits are 0)
+  auto load_keys = [&](int lo, int hi) -> float {
+    float n_out = 0.0f;
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int j = k0 + 16 * nt + kl;
-    if (j < W) {
-      const int tok = start + j;
-      int bk = trow[tok >> a.bs_shift];
-      bk = bk < 0 ? 0 : (bk >= a.NB ? a.NB - 1 : bk);
-      const char* p = kbase + (size_t)bk * blk_bytes + (size_t)(tok & bs_mask) * 256 + grp * 16;
+    for (int nt = 0; nt < NT; ++nt) {
+      const int j = lo + wave * 16 * NT + 16 * nt + kl;
+      if (j < hi) {
+        const int tok = start + j;
+        int bk = trow[tok >> a.bs_shift];
+        bk = bk < 0 ? 0 : (bk >= a.NB ? a.NB - 1 : bk);
+        const char* p = kbase + (size_t)bk * blk_bytes + (size_t)(tok & bs_mask) * 256 + grp * 16;
 #pragma unroll
-      for (int ks = 0; ks < kRKs; ++ks) kf[nt][ks] = *(const bf16x8*)(p + ks * 64);
-    } else {
-      n_inval += 1.0f;
+        for (int ks = 0; ks < kRKs; ++ks) kf[nt][ks] = *(const bf16x8*)(p + ks * 64);
+      } else {
+        n_out += 1.0f;
 #pragma unroll
-      for (int ks = 0; ks < kRKs; ++ks)
+        for (int ks = 0; ks < kRKs; ++ks)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) kf[nt][ks][e] = (__bf16)0.0f;
+          for (int e = 0; e < 8; ++e) kf[nt][ks][e] = (__bf16)0.0f;
+      }
     }
-  }
-  const bool col_wave = k0 < C;         // the wave holds keys of the compressible region
+    return n_out;
+  };
 
   // ---- query tiles: global -> registers -> LDS ring ----
   // Thread tid moves 8 bytes of a tile: row tid >> 5, bytes (tid & 31) * 8.
+  // Its row advances by 16 per tile, i.e. by 16 / G positions and 16 % G
+  // heads; the (position, head) pair is kept up to date incrementally.
   const int st_row = tid >> 5;
   const int st_off = (tid & 31) * 8;
-  auto q_addr = [&](int row) -> const char* {
+  const int di = kRRows / G, dg = kRRows - (kRRows / G) * G;
+  int ld_i = st_row / G, ld_g = st_row - (st_row / G) * G, ld_row = st_row;
+  // loads the thread's piece of the next tile in sequence (tiles 0, 1, 2, ...)
+  auto load_q = [&]() -> uint2 {
+    uint2 v = make_uint2(0u, 0u);
+    if (ld_row < rows) {
+      const int slot_i = ld_i + ring_off < W ? ld_i + ring_off : ld_i + ring_off - W;
+      v = *(const uint2*)(qbase + ((size_t)slot_i * a.Hq + ld_g) * 256 + st_off);
+    }
+    ld_row += kRRows;
+    ld_i += di;
+    ld_g += dg;
+    if (ld_g >= G) {
+      ld_g -= G;
+      ld_i += 1;
+    }
+    return v;
+  };
+  // the thread's piece of tile t (random access, for the exact route)
+  auto load_q_at = [&](int t) -> uint2 {
+    const int row = t * kRRows + st_row;
+    if (row >= rows) return make_uint2(0u, 0u);
     const int i = row / G, g = row - (row / G) * G;
     const int slot_i = i + ring_off < W ? i + ring_off : i + ring_off - W;
-    return qbase + ((size_t)slot_i * a.Hq + g) * 256;
-  };
-  auto load_q = [&](int t) -> uint2 {
-    const int row = t * kRRows + st_row;
-    if (t < n_tiles && row < rows) return *(const uint2*)(q_addr(row) + st_off);
-    return make_uint2(0u, 0u);
+    return *(const uint2*)(qbase + ((size_t)slot_i * a.Hq + g) * 256 + st_off);
   };
   auto store_q = [&](uint2 v, int t) { *(uint2*)&qbuf[t % kRQSlots][st_row * kRQStride + st_off] = v; };
   auto qfrag = [&](int t, int ks) -> bf16x8 {
     return *(const bf16x8*)&qbuf[t % kRQSlots][kl * kRQStride + ks * 64 + grp * 16];
   };
-  // 16 x (16 NT) logits of tile t: row 4 grp + r, key k0 + 16 nt + kl in acc[nt][r]
+  // Per-row input of tile t (kWithRowSums: the partial normaliser over KB1;
+  // kWeighted: 1 / Z), staged through LDS like the query tiles by threads
+  // 0..15 (0 for rows past the last one).
+  auto load_row = [&](int t) -> float {
+    const int row = t * kRRows + tid;
+    return (kStageRow && tid < kRRows && row < rows) ? zrow[row] : 0.0f;
+  };
+  auto store_row = [&](float v, int t) {
+    if (kStageRow && tid < kRRows) rowin[t % kRQSlots][tid] = v;
+  };
+  // 16 x (16 NT) logits of tile t: row 4 grp + r, key (block key) 16 NT wave + 16 nt + kl
   auto tile_mfma = [&](f32x4 (&acc)[NT], int t) {
     bf16x8 qa[kRKs];
 #pragma unroll
     for (int ks = 0; ks < kRKs; ++ks) qa[ks] = qfrag(t, ks);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+      const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
       acc[nt] = z;
     }
 #pragma unroll
@@ -199,73 +265,208 @@ __global__ __launch_bounds__(kRThreads, 2) void score_resident_kernel(ScoreArgs 
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma(qa[ks], kf[nt][ks], acc[nt]);
   };
+  // Column sums of the lane's keys over its row group, summed over the four
+  // groups and written for keys lo + ... below min(hi, C).
+  auto write_cols = [&](const float (&colacc)[NT], int lo, int hi) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      float s = colacc[nt];
+      s += __shfl_xor(s, 16);
+      s += __shfl_xor(s, 32);
+      const int j = lo + wave * 16 * NT + 16 * nt + kl;
+      if (lane < 16 && j < hi && j < C) out[j] = s;
+    }
+  };
+
+  // ============ exact route: every row's maximum as its reference ============
+  // Key blocks of kBlockKeys keys cover the window; three sweeps: row maxima,
+  // normalisers, column sums of the region's keys.
+  auto exact_unit = [&]() {
+    for (int i = tid; i < rows; i += kRThreads) {
+      refs[i] = -INFINITY;
+      zfull[i] = 0.0f;
+    }
+    for (int sweep = 0; sweep < 3; ++sweep) {
+      for (int lo = 0; lo < (sweep == 2 ? C : W); lo += kBlockKeys) {
+        const int hi = min(lo + kBlockKeys, W);
+        load_keys(lo, hi);
+        float colacc[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) colacc[nt] = 0.0f;
+        for (int t = 0; t < n_tiles; ++t) {
+          __syncthreads();
+          store_q(load_q_at(t), t);
+          __syncthreads();
+          f32x4 acc[NT];
+          tile_mfma(acc, t);
+          float ref[4], rp[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int row = t * kRRows + 4 * grp + r;
+            ref[r] = row < rows ? refs[row] : 0.0f;
+          }
+          if (sweep == 0) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              float mx = -INFINITY;
+#pragma unroll
+              for (int nt = 0; nt < NT; ++nt)
+                if (lo + wave * 16 * NT + 16 * nt + kl < hi) mx = fmaxf(mx, acc[nt][r] * c);
+              rp[r] = row_max16(mx);
+            }
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) rp[r] = 0.0f;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const bool valid = lo + wave * 16 * NT + 16 * nt + kl < hi;
+                const float e = valid ? __builtin_amdgcn_exp2f(acc[nt][r] * c - ref[r]) : 0.0f;
+                acc[nt][r] = e;
+                rp[r] += e;
+              }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) rp[r] = row_sum16(rp[r]);
+          }
+          if (sweep < 2) {
+            if (kl == 0) *(float4*)&zpart[0][wave][4 * grp] = make_float4(rp[0], rp[1], rp[2], rp[3]);
+            __syncthreads();
+            if (tid < kRRows && t * kRRows + tid < rows) {
+              const int row = t * kRRows + tid;
+              float v = zpart[0][0][tid];
+              for (int w = 1; w < kRWaves; ++w)
+                v = sweep == 0 ? fmaxf(v, zpart[0][w][tid]) : v + zpart[0][w][tid];
+              if (sweep == 0) refs[row] = fmaxf(refs[row], v);
+              else zfull[row] += v;
+            }
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int row = t * kRRows + 4 * grp + r;
+              const float w = row < rows ? 1.0f / zfull[row] : 0.0f;
+#pragma unroll
+              for (int nt = 0; nt < NT; ++nt) colacc[nt] = fmaf(acc[nt][r], w, colacc[nt]);
+            }
+          }
+        }
+        if (sweep == 2) write_cols(colacc, lo, hi);
+      }
+    }
+  };
 
   if (tid == 0) s_redo = 0;
+
+  // kWeighted: a unit whose normalisers left float's comfortable range in
+  // kWithRowSums is scored by the exact route instead (uniform branch).
+  if (MODE == kWeighted && a.uflags[unit] != 0) {
+    exact_unit();
+    return;
+  }
+
+  // ======================= fast pass: references 0 =========================
+  const int key_lo = a.key_lo, key_hi = a.key_hi;
+  const float n_inval = load_keys(key_lo, key_hi);
+  // keys past the block among the 16 lanes of the row group (logit 0, exp2 = 1)
+  const float inval16 = row_sum16(n_inval);
+  const bool col_wave = kCols && key_lo + wave * 16 * NT < C;   // the wave holds region keys
   float colacc[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) colacc[nt] = 0.0f;
-
-  // ======================= fast pass: references 0 =========================
+  bool bad = false;
   {
-    store_q(load_q(0), 0);
-    store_q(load_q(1), 1);
-    uint2 stg0 = load_q(2), stg1 = load_q(3);
+    store_q(load_q(), 0);
+    store_q(load_q(), 1);
+    store_row(load_row(0), 0);
+    store_row(load_row(1), 1);
+    uint2 stg0 = load_q();
+    uint2 stg1 = load_q();
+    float sr0 = load_row(2), sr1 = load_row(3);
     __syncthreads();
     f32x4 acc0[NT], acc1[NT];
     tile_mfma(acc0, 0);
-    bool bad = false;
     // One tile: `cur` holds its logits, the next tile's go into `nxt`; `stg`
-    // carries tile t + 2 to its LDS slot and then fetches tile t + 4.
-    auto step = [&](f32x4 (&cur)[NT], f32x4 (&nxt)[NT], uint2& stg, int t) {
+    // and `sr` carry tile t + 2's query piece and row input to their LDS
+    // slots and then fetch tile t + 4's.
+    auto step = [&](f32x4 (&cur)[NT], f32x4 (&nxt)[NT], uint2& stg, float& sr, int t) {
       store_q(stg, t + 2);
-      stg = load_q(t + 4);
+      stg = load_q();
+      store_row(sr, t + 2);
+      sr = load_row(t + 4);
       // The next tile's logits (past the last tile: zero rows, never used) on
-      // the matrix cores while this tile's exponentials run: eight regions
-      // fenced against reordering, each issuing NT / 2 independent MFMAs (the
-      // same reduction step of different N-tiles) and NT / 2 of the lane's
-      // 4 NT exponentials, so the wave issues VALU work while its own MFMAs
-      // execute.
+      // the matrix cores while this tile's VALU work runs, in regions fenced
+      // against reordering: one region per logit of the lane (its multiply,
+      // exp2 and add) carries one of the first 3 NT MFMAs (reduction steps
+      // 0-2; consecutive ones update different N-tiles); the last step's
+      // MFMAs are issued while the normalisers' LDS reads are in flight.  A
+      // wave thus issues VALU work while its own MFMAs execute.
       bf16x8 qa[kRKs];
 #pragma unroll
       for (int ks = 0; ks < kRKs; ++ks) qa[ks] = qfrag(t + 1, ks);
+      float rp[4];
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-        nxt[nt] = z;
-      }
-      float rp[4] = {-n_inval, -n_inval, -n_inval, -n_inval};
-      constexpr int kPer = NT / 2;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-#pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-          const int mi = i * kPer + j, ks = mi / NT, nt = mi % NT;
-          nxt[nt] = mfma(qa[ks], kf[nt][ks], nxt[nt]);
+      for (int k = 0; k < 4 * NT; ++k) {
+        if (k < 3 * NT) {
+          const int ks = k / NT, nt = k % NT;
+          if (ks == 0) {
+            const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+            nxt[nt] = mfma(qa[0], kf[nt][0], z);
+          } else {
+            nxt[nt] = mfma(qa[ks], kf[nt][ks], nxt[nt]);
+          }
         }
-#pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-          const int e = i * kPer + j, nt = e / 4, r = e % 4;
+        {
+          const int nt = k / 4, r = k % 4;
           const float x = __builtin_amdgcn_exp2f(cur[nt][r] * c);
           cur[nt][r] = x;
-          rp[r] += x;
+          if (kRowSumsHere) rp[r] = nt == 0 ? x : rp[r] + x;
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) rp[r] = row_sum16(rp[r]);
       float* zp = &zpart[t & 1][0][0];
-      if (kl == 0) *(float4*)&zp[wave * kRRows + 4 * grp] = make_float4(rp[0], rp[1], rp[2], rp[3]);
+      if (kRowSumsHere) {
+        // this wave's sum of row 4 grp + (kl >> 2), published by one lane of each quad
+        const float zw = row_sums16_transposed(rp, kl) - inval16;
+        if ((kl & 3) == 0) zp[wave * kRRows + 4 * grp + (kl >> 2)] = zw;
+      }
       __syncthreads();
-      // the tile's normalisers: lane (grp, 4 m + q) adds waves 2q, 2q + 1 of row 4 grp + m
-      const int m = 4 * grp + ((lane >> 2) & 3);
-      const int q2 = 2 * (lane & 3);
-      const float z = quad_sum(zp[q2 * kRRows + m] + zp[(q2 + 1) * kRRows + m]);
-      const bool row_ok = t * kRRows + m < rows;
-      bad = bad || (row_ok && !(z >= 0x1p-40f && z <= 0x1p100f));
-      const float wm = row_ok ? __builtin_amdgcn_rcpf(z) : 0.0f;
-      if (col_wave) {
-        const float w0 = row_bcast<0>(wm), w1 = row_bcast<1>(wm), w2 = row_bcast<2>(wm),
-                    w3 = row_bcast<3>(wm);
+      float wm = 0.0f;
+      if (kRowSumsHere) {
+        // the tile's normalisers: lane (grp, 4 m + q) adds waves 2q, 2q + 1 of row 4 grp + m
+        const int m = 4 * grp + ((lane >> 2) & 3);
+        const int q2 = 2 * (lane & 3);
+        const float za = zp[q2 * kRRows + m], zb = zp[(q2 + 1) * kRRows + m];
+        const float zx = MODE == kWithRowSums ? rowin[t % kRQSlots][m] : 0.0f;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) nxt[nt] = mfma(qa[3], kf[nt][3], nxt[nt]);
+        __builtin_amdgcn_sched_barrier(0);
+        const float z = quad_sum(za + zb) + zx;
+        const bool row_ok = t * kRRows + m < rows;
+        if (MODE != kRowSums) bad |= __ballot(row_ok && !(z >= 0x1p-40f && z <= 0x1p100f)) != 0;
+        if (MODE == kRowSums) {
+          if (wave == 0 && (lane & 3) == 0 && row_ok) zrow[t * kRRows + m] = z;
+        } else {
+          wm = row_ok ? __builtin_amdgcn_rcpf(z) : 0.0f;
+          if (MODE == kWithRowSums && wave == 0 && (lane & 3) == 0 && row_ok) zrow[t * kRRows + m] = wm;
+        }
+      } else {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) nxt[nt] = mfma(qa[3], kf[nt][3], nxt[nt]);
+      }
+      if (kCols && col_wave) {
+        float w0, w1, w2, w3;
+        if (kRowSumsHere) {
+          w0 = row_bcast<0>(wm);
+          w1 = row_bcast<1>(wm);
+          w2 = row_bcast<2>(wm);
+          w3 = row_bcast<3>(wm);
+        } else {
+          const float4 w = *(const float4*)&rowin[t % kRQSlots][4 * grp];
+          w0 = w.x;
+          w1 = w.y;
+          w2 = w.z;
+          w3 = w.w;
+        }
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           float s = colacc[nt];
@@ -278,112 +479,64 @@ __global__ __launch_bounds__(kRThreads, 2) void score_resident_kernel(ScoreArgs 
       }
     };
     for (int t = 0; t < n_tiles; t += 2) {
-      step(acc0, acc1, stg0, t);
-      if (t + 1 < n_tiles) step(acc1, acc0, stg1, t + 1);
-    }
-    if (__ballot(bad) && lane == 0) s_redo = 1;
-    __syncthreads();
-  }
-
-  // ============ exact rerun: every row's maximum as its reference ============
-  if (s_redo) {                         // uniform over the workgroup
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) colacc[nt] = 0.0f;
-    const bool keep_refs = rows <= kRMaxRefRows;
-    for (int pass = 0; pass < 2; ++pass) {
-      for (int t = 0; t < n_tiles; ++t) {
-        __syncthreads();
-        store_q(load_q(t), t);
-        __syncthreads();
-        f32x4 acc[NT];
-        tile_mfma(acc, t);
-        float rp[4];
-        if (pass == 0) {
-          // the row maxima over this wave's keys, then over the workgroup
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float mx = -INFINITY;
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-              if (k0 + 16 * nt + kl < W) mx = fmaxf(mx, acc[nt][r] * c);
-            rp[r] = row_max16(mx);
-          }
-          if (kl == 0) *(float4*)&zpart[0][wave][4 * grp] = make_float4(rp[0], rp[1], rp[2], rp[3]);
-          __syncthreads();
-          if (tid < kRRows) {
-            float mx = zpart[0][0][tid];
-            for (int w = 1; w < kRWaves; ++w) mx = fmaxf(mx, zpart[0][w][tid]);
-            if (keep_refs) refs[t * kRRows + tid] = mx;
-          }
-          continue;
-        }
-        float ref[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = t * kRRows + 4 * grp + r;
-          ref[r] = (keep_refs && row < rows) ? refs[row] : 0.0f;
-          rp[r] = 0.0f;
-        }
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const bool valid = k0 + 16 * nt + kl < W;
-            const float e = valid ? __builtin_amdgcn_exp2f(acc[nt][r] * c - ref[r]) : 0.0f;
-            acc[nt][r] = e;
-            rp[r] += e;
-          }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) rp[r] = row_sum16(rp[r]);
-        if (kl == 0) *(float4*)&zpart[0][wave][4 * grp] = make_float4(rp[0], rp[1], rp[2], rp[3]);
-        __syncthreads();
-        const int m = 4 * grp + ((lane >> 2) & 3);
-        const int q2 = 2 * (lane & 3);
-        const float z = quad_sum(zpart[0][q2][m] + zpart[0][q2 + 1][m]);
-        const float wm = (t * kRRows + m < rows) ? 1.0f / z : 0.0f;
-        const float w0 = row_bcast<0>(wm), w1 = row_bcast<1>(wm), w2 = row_bcast<2>(wm),
-                    w3 = row_bcast<3>(wm);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-          colacc[nt] += acc[nt][0] * w0 + acc[nt][1] * w1 + acc[nt][2] * w2 + acc[nt][3] * w3;
-      }
+      step(acc0, acc1, stg0, sr0, t);
+      if (t + 1 < n_tiles) step(acc1, acc0, stg1, sr1, t + 1);
     }
   }
 
-  // ---- column sums: the four row groups of each key, written for keys < C ----
-  float* out = a.out + (size_t)unit * C;
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    float s = colacc[nt];
-    s += __shfl_xor(s, 16);
-    s += __shfl_xor(s, 32);
-    const int j = k0 + 16 * nt + kl;
-    if (lane < 16 && j < C) out[j] = s;
+  if (MODE == kRowSums) return;
+  if (bad && lane == 0) s_redo = 1;
+  __syncthreads();
+  if (MODE == kWithRowSums) {
+    // the next launch reruns units whose normalisers left the range exactly
+    if (tid == 0) a.uflags[unit] = s_redo;
+    write_cols(colacc, key_lo, key_hi);
+    return;
   }
+  if (MODE == kWhole && s_redo) {       // uniform over the workgroup
+    exact_unit();
+    return;
+  }
+  write_cols(colacc, key_lo, key_hi);
 }
 
-template <int NT>
-hipError_t launch_nt(const ScoreArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((score_resident_kernel<NT>), dim3((unsigned)a.n_units), dim3(kRThreads), 0, stream, a);
+template <int NT, int MODE>
+hipError_t launch_one(const ScoreArgs& a, int lo, int hi, hipStream_t stream) {
+  ScoreArgs b = a;
+  b.key_lo = lo;
+  b.key_hi = hi;
+  hipLaunchKernelGGL((score_resident_kernel<NT, MODE>), dim3((unsigned)a.n_units), dim3(kRThreads), 0, stream, b);
   return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t launch_mode(const ScoreArgs& a, int lo, int hi, hipStream_t stream) {
+  switch (resident_tiles(hi - lo)) {
+    case 2: return launch_one<2, MODE>(a, lo, hi, stream);
+    case 4: return launch_one<4, MODE>(a, lo, hi, stream);
+    case 6: return launch_one<6, MODE>(a, lo, hi, stream);
+    default: return launch_one<8, MODE>(a, lo, hi, stream);
+  }
 }
 
 }  // namespace
 
-int resident_tiles(int W) {
-  const int per_wave = (W + kRWaves - 1) / kRWaves;
+int resident_tiles(int n_keys) {
+  const int per_wave = (n_keys + kRWaves - 1) / kRWaves;
   const int nt = (per_wave + 15) / 16;
   return nt <= 2 ? 2 : (nt <= 4 ? 4 : (nt <= 6 ? 6 : 8));
 }
 
 hipError_t launch_score_resident(const ScoreArgs& a, hipStream_t stream) {
   if (a.n_units == 0) return hipSuccess;
-  switch (resident_tiles(a.W)) {
-    case 2: return launch_nt<2>(a, stream);
-    case 4: return launch_nt<4>(a, stream);
-    case 6: return launch_nt<6>(a, stream);
-    default: return launch_nt<8>(a, stream);
-  }
+  if (a.W <= kResidentBlock) return launch_mode<kWhole>(a, 0, a.W, stream);
+  if (!a.zrow || !a.uflags) return hipErrorInvalidValue;
+  hipError_t e;
+  if ((e = launch_mode<kRowSums>(a, kResidentBlock, a.W, stream)) != hipSuccess) return e;
+  if ((e = launch_mode<kWithRowSums>(a, 0, kResidentBlock, stream)) != hipSuccess) return e;
+  // KB1's region keys (none if C <= 1024: the launch then only runs the exact route where flagged)
+  const int hi = a.C > kResidentBlock ? a.C : kResidentBlock + 1;
+  return launch_mode<kWeighted>(a, kResidentBlock, hi, stream);
 }
 
 }  // namespace kara

@@ -65,6 +65,18 @@ SCORE_CASES = {
     "resident-w17-b0": dict(n_seqs=3, n_layers=2, n_q_heads=6, n_kv_heads=3, head_dim=128, block_size=8,
                             window=17, protect=0, top_k=3, budget=9, lens=(17, 90), dtype=torch.bfloat16,
                             qk_std=0.5),
+    # windows over two key blocks (1024 + the rest): region inside the first
+    # block (C = 900), region equal to the window (B = 0, C = 2048), a short
+    # second block with G = 3
+    "resident-w1500-c900": dict(n_seqs=2, n_layers=1, n_q_heads=8, n_kv_heads=2, head_dim=128, block_size=16,
+                                window=1500, protect=600, top_k=50, budget=200, lens=(1500, 4000),
+                                dtype=torch.bfloat16, qk_std=0.3),
+    "resident-w2048-b0-g2": dict(n_seqs=1, n_layers=2, n_q_heads=4, n_kv_heads=2, head_dim=128, block_size=16,
+                                 window=2048, protect=0, top_k=128, budget=600, lens=[2500],
+                                 dtype=torch.bfloat16, qk_std=0.25),
+    "resident-w1100-g3": dict(n_seqs=2, n_layers=1, n_q_heads=6, n_kv_heads=2, head_dim=128, block_size=16,
+                              window=1100, protect=50, top_k=60, budget=300, lens=(1100, 3000),
+                              dtype=torch.bfloat16, qk_std=0.4),
 }
 
 
@@ -87,15 +99,16 @@ def test_score_stage(name):
     say(name, "max rel err", worst)
 
 
-def test_score_stage_exact_fallback():
+@pytest.mark.parametrize("window", [256, 1600])
+def test_score_stage_exact_fallback(window):
     """One key made ~110 nats more attractive to one query than that query's
     first keys: with the first keys' maximum as the row's reference the sum
     would overflow float, so the workgroup must redo its row statistics with a
     running maximum.  The scores still match the oracle."""
     say("score stage exact fallback")
     wl = gpu_workload(None, n_seqs=2, n_layers=1, n_q_heads=8, n_kv_heads=2, head_dim=128, block_size=16,
-                      window=256, protect=32, top_k=8, budget=40, lens=[300, 700], dtype=torch.bfloat16,
-                      qk_std=0.1)
+                      window=window, protect=32, top_k=8, budget=40, lens=[window + 44, window + 444],
+                      dtype=torch.bfloat16, qk_std=0.1)
     b, i, j = 0, 150, 200                      # sequence, query position, key position (window-local)
     q = wl.q_window[b, 0, i, 0].float()        # query head 0 belongs to KV head 0
     s = 110.0 * math.sqrt(128) / float(q @ q)
@@ -114,14 +127,15 @@ def test_score_stage_exact_fallback():
     assert orc[0, j] > 0.9                     # the planted key took that row's whole weight
 
 
-def test_score_stage_exact_rerun_for_very_negative_logits():
+@pytest.mark.parametrize("window", [256, 2048])
+def test_score_stage_exact_rerun_for_very_negative_logits(window):
     """One query row whose logits with every window key are about -60 nats:
     without a reference its normaliser falls below float's comfortable range,
     so the scorer must take the exact route (every row's maximum as its
     reference).  The scores still match the oracle."""
     say("score stage exact rerun, very negative logits")
     wl = gpu_workload(None, n_seqs=1, n_layers=1, n_q_heads=4, n_kv_heads=1, head_dim=128, block_size=16,
-                      window=256, protect=32, top_k=8, budget=40, lens=[600], dtype=torch.bfloat16,
+                      window=window, protect=32, top_k=8, budget=40, lens=[window + 344], dtype=torch.bfloat16,
                       qk_std=0.1)
     L = int(wl.lens[0])
     toks = torch.arange(L - wl.window, L)
@@ -233,6 +247,8 @@ E2E_CASES = {
                            window=96, protect=16, top_k=20, budget=7, lens=(96, 200), dtype=torch.bfloat16,
                            qk_std=0.5),
     "resident-w1000-g5": SCORE_CASES["resident-w1000-g5"],
+    "resident-w1500-c900": SCORE_CASES["resident-w1500-c900"],
+    "resident-w2048-b0-g2": SCORE_CASES["resident-w2048-b0-g2"],
 }
 
 
