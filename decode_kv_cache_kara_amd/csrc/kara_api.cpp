@@ -124,16 +124,27 @@ struct Plan {
   std::vector<int32_t> freed;   // old tail ids, sequences in call order, positions ascending
 };
 
+// One sequence's compaction plan: the boundary block's table position, the
+// fresh blocks its compacted tail takes, and its new length L - C + R.
+struct SeqPlan {
+  int64_t f0, n_fresh, new_len;
+};
+
+SeqPlan plan_sequence(int64_t L, const kara_params* p, int bs) {
+  SeqPlan q;
+  q.f0 = (L - p->window) / bs;
+  q.n_fresh = ceil_div((L - p->window) % bs + p->budget + p->protect, bs);
+  q.new_len = L - (p->window - p->protect) + p->budget;
+  return q;
+}
+
 // Fills the new tables and lengths from the front of the pool without popping.
 kara_status make_plan(const kara_shape* sh, const kara_params* p, int32_t n_seqs,
                       const int32_t* table_h, int32_t max_blocks, const int32_t* lens_h,
                       const kara_pool* pool, int32_t* new_table_h, int32_t* new_lens_h, Plan* plan) {
   const int bs = sh->block_size;
   int64_t need = 0;
-  for (int32_t b = 0; b < n_seqs; ++b) {
-    const int64_t L = lens_h[b];
-    need += ceil_div((L - p->window) % bs + p->budget + p->protect, bs);
-  }
+  for (int32_t b = 0; b < n_seqs; ++b) need += plan_sequence(lens_h[b], p, bs).n_fresh;
   if (need > (int64_t)pool->fifo.size())
     return fail(KARA_E_NOBLOCKS, "need %lld fresh blocks, pool has %zu", (long long)need, pool->fifo.size());
   if (!new_table_h || !new_lens_h) return fail(KARA_E_INVAL, "host outputs NULL");
@@ -141,15 +152,13 @@ kara_status make_plan(const kara_shape* sh, const kara_params* p, int32_t n_seqs
   plan->freed.clear();
   size_t cur = 0;
   for (int32_t b = 0; b < n_seqs; ++b) {
-    const int64_t L = lens_h[b];
-    const int64_t f0 = (L - p->window) / bs;
-    const int64_t n_new = ceil_div((L - p->window) % bs + p->budget + p->protect, bs);
+    const SeqPlan q = plan_sequence(lens_h[b], p, bs);
     const int32_t* row = table_h + (size_t)b * max_blocks;
     int32_t* out = new_table_h + (size_t)b * max_blocks;
-    for (int64_t e = 0; e < f0; ++e) out[e] = row[e];
-    for (int64_t e = 0; e < n_new; ++e) out[f0 + e] = plan->fresh[cur++];
-    for (int64_t e = f0 + n_new; e < max_blocks; ++e) out[e] = -1;
-    new_lens_h[b] = (int32_t)(L - (p->window - p->protect) + p->budget);
+    for (int64_t e = 0; e < q.f0; ++e) out[e] = row[e];
+    for (int64_t e = 0; e < q.n_fresh; ++e) out[q.f0 + e] = plan->fresh[cur++];
+    for (int64_t e = q.f0 + q.n_fresh; e < max_blocks; ++e) out[e] = -1;
+    new_lens_h[b] = (int32_t)q.new_len;
   }
   for (int32_t b = 0; b < n_seqs; ++b) {
     const int64_t L = lens_h[b];
@@ -369,6 +378,9 @@ kara_status compress_impl(const kara_shape* shape, const kara_params* params, in
   if (n_seqs == 0) return KARA_OK;
   if (qs.ring && (qs.ring->n_slots < 1 || !qs.ring->slots_d || !qs.ring->counts_d))
     return fail(KARA_E_INVAL, "query ring: n_slots < 1 or slot/count arrays NULL");
+  if (qs.ring && qs.ring->window != params->window)
+    return fail(KARA_E_INVAL, "query ring holds windows of %d, the call compresses windows of %d",
+                qs.ring->window, params->window);
   if (!q_window || !kv_pool || !block_table_d || !seq_lens_d || !new_block_table_d)
     return fail(KARA_E_INVAL, "device pointer NULL");
   if (!is_aligned(q_window, 16) || !is_aligned(kv_pool, 16))
@@ -475,6 +487,9 @@ kara_status kara_append(const kara_shape* shape, int32_t window, int32_t n_seqs,
     return fail(KARA_E_INVAL, "layer %d outside [-1, %d)", layer, shape->n_layers);
   if (n_blocks < 1 || max_blocks < 1) return fail(KARA_E_INVAL, "n_blocks and max_blocks must be >= 1");
   if (!ring || ring->n_slots < 1) return fail(KARA_E_INVAL, "query ring NULL or without slots");
+  if (ring->window != window)
+    return fail(KARA_E_INVAL, "query ring holds windows of %d, the call appends with window %d", ring->window,
+                window);
   if (n_seqs == 0) return KARA_OK;
   if (!q_d || !k_d || !v_d || !kv_pool || !block_table_d || !positions_d || !ring->q_ring ||
       !ring->slots_d || !ring->counts_d)
@@ -681,6 +696,26 @@ kara_status kara_paged_compact(const kara_shape* shape, const kara_params* param
                                       new_block_table_d, max_blocks, seq_lens_d, retained_d);
   if ((e = kara::launch_compact(ca, s)) != hipSuccess) return hip_fail(e, "compact launch");
   commit_plan(pool, plan);
+  return KARA_OK;
+}
+
+kara_status kara_plan_lengths(const kara_params* params, int32_t block_size, int32_t n_seqs,
+                              const int32_t* seq_lens_h, int32_t* new_lens_out, int32_t* fresh_blocks_out) {
+  kara_status st;
+  if ((st = check_params(params)) != KARA_OK) return st;
+  if (block_size < 1 || block_size > 1024 || (block_size & (block_size - 1)) != 0)
+    return fail(KARA_E_UNSUPPORTED, "block_size %d is not a power of two <= 1024", block_size);
+  if (n_seqs < 0) return fail(KARA_E_INVAL, "n_seqs < 0");
+  if (n_seqs > 0 && (!seq_lens_h || !new_lens_out || !fresh_blocks_out))
+    return fail(KARA_E_INVAL, "plan arrays NULL");
+  for (int32_t b = 0; b < n_seqs; ++b)
+    if (seq_lens_h[b] < params->window)
+      return fail(KARA_E_INVAL, "sequence %d: length %d < window %d", b, seq_lens_h[b], params->window);
+  for (int32_t b = 0; b < n_seqs; ++b) {
+    const SeqPlan q = plan_sequence(seq_lens_h[b], params, block_size);
+    new_lens_out[b] = (int32_t)q.new_len;
+    fresh_blocks_out[b] = (int32_t)q.n_fresh;
+  }
   return KARA_OK;
 }
 

@@ -50,7 +50,7 @@ class kara_params(ctypes.Structure):
 
 
 class kara_query_ring(ctypes.Structure):
-    _fields_ = [("q_ring", ctypes.c_void_p), ("n_slots", ctypes.c_int32),
+    _fields_ = [("q_ring", ctypes.c_void_p), ("n_slots", ctypes.c_int32), ("window", ctypes.c_int32),
                 ("slots_d", ctypes.c_void_p), ("counts_d", ctypes.c_void_p)]
 
 
@@ -102,6 +102,7 @@ _SIGS = {
     "kara_token2chunk": (_I, [_I, _I, _I, _I, _P, _P, _P, _P]),
     "kara_paged_compact": (_I, [_P, _P, _I, _P, _I, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
     "kara_schedule_step": (_I, [ctypes.c_int64, _I, _I, _I, _P, _P, _P, _P, _P]),
+    "kara_plan_lengths": (_I, [_P, _I, _I, _P, _P, _P]),
     "kara_append": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _I, _P, _I, _P, _P, _P]),
     "kara_compress_ring": (_I, [_P, _P, _I, _P, _P, _I, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P,
                                 ctypes.c_size_t, _P, _P, _P, _P, _P]),
@@ -334,14 +335,25 @@ def kara_schedule_step(step, period, window, seq_lens, watermarks, selected):
     return out[:nb.value].tolist()
 
 
+def kara_plan_lengths(params, block_size, seq_lens):
+    """Host-only plan: (new lengths, fresh blocks per sequence) as int32 CPU
+    tensors, the arithmetic kara_compress uses (include/kara.h)."""
+    n = seq_lens.numel()
+    new_lens = torch.empty(n, dtype=torch.int32)
+    fresh = torch.empty(n, dtype=torch.int32)
+    _check(_lib.kara_plan_lengths(ctypes.byref(params), int(block_size), n, _host_i32(seq_lens, "seq_lens"),
+                                  new_lens.data_ptr(), fresh.data_ptr()))
+    return new_lens, fresh
+
+
 class QueryRing:
     """Device ring of every sequence slot's last W query states (see
     kara_query_ring in include/kara.h): q [n_slots][Lyr][W][Hq][D]."""
 
     def __init__(self, q, slots_d, counts_d):
         self.q, self.slots_d, self.counts_d = q, slots_d, counts_d
-        self.struct = kara_query_ring(_dev(q, "q_ring"), q.shape[0], _dev(slots_d, "slots_d", torch.int32),
-                                      _dev(counts_d, "counts_d", torch.int32))
+        self.struct = kara_query_ring(_dev(q, "q_ring"), q.shape[0], q.shape[2],
+                                      _dev(slots_d, "slots_d", torch.int32), _dev(counts_d, "counts_d", torch.int32))
 
 
 def kara_append(shape, window, layer, q, k, v, kv_pool, block_table_d, positions_d, ring, stream=None):

@@ -67,28 +67,32 @@ class TraceConfig:
 
 def simulate_schedule(cfg: TraceConfig):
     """Host-only replay of the selection and eligibility decisions, used to
-    size the block pool before any GPU memory is touched.  Returns
-    (n_events, peak blocks in use, largest per-event fresh-block demand)."""
+    size the block pool before any GPU memory is touched: the library's own
+    schedule (kara_schedule_step) and plan (kara_plan_lengths) on the lengths
+    the trace will have.  Returns (n_events, peak blocks in use, largest
+    per-event fresh-block demand)."""
     rng = np.random.default_rng(cfg.seed)
-    S, bs = cfg.n_seqs, cfg.block_size
-    W, B, R, P = cfg.window, cfg.protect, cfg.budget, cfg.period
+    S, bs, P = cfg.n_seqs, cfg.block_size, cfg.period
+    params = kara.kara_params(cfg.window, cfg.protect, cfg.top_k, cfg.budget)
     phys = np.full(S, cfg.init_len, dtype=np.int64)
     wm = np.zeros(S, dtype=np.int64)
     logical = cfg.init_len
-    n_events, peak, fresh_max = 0, 0, 0
+    n_events, peak, fresh_max, step = 0, 0, 0, 0
     while logical < cfg.max_len and (cfg.max_events == 0 or n_events < cfg.max_events):
         phys += P
         logical += P
+        step += P
         n_events += 1
         peak = max(peak, int(sum(-(-L // bs) for L in phys)))
-        sel = rng.random(S) < cfg.select_prob
-        fresh = 0
-        for b in range(S):
-            if sel[b] and phys[b] - wm[b] >= W:
-                fresh += -(-(((phys[b] - W) % bs) + R + B) // bs)
-                phys[b] = phys[b] - (W - B) + R
-                wm[b] = phys[b] - B
-        fresh_max = max(fresh_max, fresh)
+        sel = (rng.random(S) < cfg.select_prob).astype(np.uint8)
+        batch = kara.kara_schedule_step(step, P, cfg.window, torch.from_numpy(phys.astype(np.int32)),
+                                        torch.from_numpy(wm.astype(np.int32)), torch.from_numpy(sel))
+        if not batch:
+            continue
+        new_lens, fresh = kara.kara_plan_lengths(params, bs, torch.tensor(phys[batch], dtype=torch.int32))
+        fresh_max = max(fresh_max, int(fresh.sum()))
+        phys[batch] = new_lens.numpy()
+        wm[batch] = phys[batch] - cfg.protect
     return n_events, peak, fresh_max
 
 

@@ -115,11 +115,17 @@ typedef struct {
   int32_t flags;
 } kara_params;
 
-/* Host free list of block ids: allocation pops the front, freeing pushes the
- * back (first in, first out), so block assignment is deterministic. */
+/* Host free list of the paged cache's block ids (the paper's Abstract adapts
+ * the method to PagedAttention; "Technical Summary: Kara", Methodology 3:
+ * compression rewrites the trailing blocks of a sequence and frees what they
+ * held).  Allocation pops the front, freeing pushes the back (first in, first
+ * out), so block assignment is deterministic.  The pool object is host memory
+ * owned by the library (create / destroy); ids refer to blocks of the
+ * caller's device cache. */
 typedef struct kara_pool kara_pool;
 
-/* Message for the calling thread's last non-OK status ("" if none). */
+/* Message for the calling thread's last non-OK status ("" if none); the
+ * string is owned by the library and valid until the thread's next call. */
 const char* kara_last_error(void);
 
 /* Library version string. */
@@ -148,7 +154,12 @@ int32_t kara_pool_snapshot(const kara_pool* pool, int32_t* ids_out, int32_t cap)
 void kara_pool_destroy(kara_pool* pool);
 
 /* Device workspace bytes that kara_compress and kara_score need for n_seqs
- * sequences of this shape (0 on invalid arguments). */
+ * sequences of this shape (0 on invalid arguments): the scorer's column sums
+ * of every unit ("Technical Summary: Kara", Methodology 1: scores accumulated
+ * over all window queries), for windows of more than 1024 keys one float per
+ * (unit, query row) and one flag per unit, and the kept positions of every
+ * unit (Methodology 2).  The caller allocates it (256-byte aligned) and owns
+ * it; the library keeps no pointer past the call's stream order. */
 size_t kara_workspace_bytes(const kara_shape* shape, const kara_params* params, int32_t n_seqs);
 
 /* Whole step for n_seqs sequences (the selected ones, in call order).
@@ -281,6 +292,9 @@ kara_status kara_compress_static(const kara_shape* shape, const kara_params* par
  * over everything the sequence has produced, whether or not it was later
  * compacted away) sits at ring position n mod W.
  *   q_ring    dev [n_slots][n_layers][W][n_q_heads][head_dim] (dtype)
+ *   n_slots   ring rows
+ *   window    W the ring was built with; kara_compress_ring and kara_append
+ *             reject a call whose window differs (KARA_E_INVAL)
  *   slots_d   dev [n_seqs] ring row of each sequence of the call
  *   counts_d  dev [n_seqs] tokens produced so far: for kara_compress_ring the
  *             count N, so the window is tokens N - W .. N - 1; for
@@ -292,6 +306,7 @@ kara_status kara_compress_static(const kara_shape* shape, const kara_params* par
 typedef struct {
   void* q_ring;
   int32_t n_slots;
+  int32_t window;
   const int32_t* slots_d;
   const int32_t* counts_d;
 } kara_query_ring;
@@ -370,6 +385,18 @@ kara_status kara_decode_attention(const kara_shape* shape, int32_t n_seqs, int32
 kara_status kara_schedule_step(int64_t step, int32_t period, int32_t window, int32_t n_seqs,
                                const int32_t* seq_lens, const int32_t* watermarks,
                                const uint8_t* selected, int32_t* batch_out, int32_t* n_batch);
+
+/* Host-only plan of a compression step for callers that size pools or
+ * simulate schedules ("Technical Summary: Kara", Methodology 3: the trailing
+ * blocks of a compressed sequence are replaced, the rest of its table is
+ * kept).  For each sequence b (seq_lens_h[b] >= W): new_lens_out[b] =
+ * seq_lens_h[b] - C + R, the length kara_compress returns, and
+ * fresh_blocks_out[b] = ceil((p_b + R + B) / block_size) with
+ * p_b = (seq_lens_h[b] - W) mod block_size, the fresh blocks it pops for b.
+ * The same arithmetic as kara_compress's own plan; touches no pool.
+ * KARA_E_INVAL / KARA_E_UNSUPPORTED on bad arguments (nothing written). */
+kara_status kara_plan_lengths(const kara_params* params, int32_t block_size, int32_t n_seqs,
+                              const int32_t* seq_lens_h, int32_t* new_lens_out, int32_t* fresh_blocks_out);
 
 /* ------------------------------------------------------------------------
  * Serving-policy simulator (host only).  Periodic window compression against

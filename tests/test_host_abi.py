@@ -234,3 +234,58 @@ def test_compress_static_rejects_oversized_batch_before_side_effects():
     assert st == kara.KARA_E_WORKSPACE
     assert "static scratch" in kara.kara_last_error()
     assert pool.snapshot() == list(range(20))
+
+
+def _ring(window, n_slots=2):
+    return kara.kara_query_ring(FAKE * 16, n_slots, window, FAKE * 16, FAKE * 16)
+
+
+def test_ring_window_must_match_the_call():
+    """A query ring records the window it was built with; appending or
+    compressing with another window is rejected before anything is touched
+    (the ring's rows would otherwise be indexed past their end)."""
+    sh = shape()
+    ring = _ring(window=16)
+    st = kara.lib.kara_append(ctypes.byref(sh), 8, 1, 0, FAKE * 16, FAKE * 16, FAKE * 16, FAKE * 16, 20,
+                              FAKE * 16, 5, FAKE * 16, ctypes.byref(ring), None)
+    assert st == kara.KARA_E_INVAL and "window" in kara.kara_last_error()
+    c = Call()
+    before = c.pool.snapshot()
+    st = kara.lib.kara_compress_ring(
+        ctypes.byref(c.shape), ctypes.byref(c.params), len(c.lens), ctypes.byref(_ring(window=c.params.window + 1)),
+        FAKE * 16, c.n_blocks, c.table, FAKE * 16, c.max_blocks, _i32(c.lens), FAKE * 16, c.pool.handle,
+        c.new_table, FAKE * 16, c.new_lens, 256 * 16, c.ws, None, None, None, None, None)
+    assert st == kara.KARA_E_INVAL and "window" in kara.kara_last_error()
+    assert c.pool.snapshot() == before
+    assert list(c.new_lens) == [0, 0]
+
+
+def test_plan_lengths_match_the_oracle_plan():
+    """kara_plan_lengths (the library's own per-sequence plan) against the
+    oracle's plan_compaction: new lengths and fresh blocks taken per sequence."""
+    import numpy as np
+    import torch
+
+    from oracle import kara_oracle as ko
+    rng = np.random.default_rng(11)
+    for trial in range(30):
+        bs = int(2 ** rng.integers(0, 7))
+        W = int(rng.integers(1, 600))
+        B = int(rng.integers(0, W))
+        C = W - B
+        R = int(rng.integers(1, C + 1))
+        K = int(rng.integers(1, C + 1))
+        lens = rng.integers(W, W + 3000, size=int(rng.integers(0, 12)))
+        MB = int(max([-(-int(L) // bs) for L in lens] + [1])) + 8
+        table = np.arange(len(lens) * MB).reshape(len(lens), MB)
+        fifo = ko.FifoPool(range(10 ** 6, 10 ** 6 + 10 ** 5))
+        want_table, want_lens = ko.plan_compaction(table, lens, W, B, R, bs, fifo)
+        new_lens, fresh = kara.kara_plan_lengths(kara.kara_params(W, B, K, R), bs,
+                                                  torch.tensor(lens, dtype=torch.int32))
+        assert new_lens.tolist() == want_lens.tolist()
+        taken = [int((row >= 10 ** 6).sum()) for row in want_table]
+        assert fresh.tolist() == taken
+    with pytest.raises(kara.KaraError):
+        kara.kara_plan_lengths(kara.kara_params(8, 2, 2, 3), 3, torch.tensor([10], dtype=torch.int32))
+    with pytest.raises(kara.KaraError):
+        kara.kara_plan_lengths(kara.kara_params(8, 2, 2, 3), 4, torch.tensor([7], dtype=torch.int32))
