@@ -49,9 +49,45 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash(name):
-    with open(os.path.join(ROOT, "decode_kv_cache_kara_amd", "csrc", name), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+SCORE_SOURCES = ("kara_score_resident.hip", "kara_score_kernel.hpp")
+
+
+def kernel_source_hash(names=SCORE_SOURCES):
+    """sha256 prefix of the scoring kernels' sources (both scorers)."""
+    h = hashlib.sha256()
+    for name in names:
+        with open(os.path.join(ROOT, "decode_kv_cache_kara_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def score_path(wl, flags):
+    """Which scorer the library runs for this workload (the selection rule of
+    the library's kara_internal.hpp, restated) and its executed logits per
+    (sequence, layer): 'resident' scores with the window's keys in registers
+    (16-row query tiles, one extra tile of MFMAs at the end of each launch;
+    blocks of up to 1024 keys, 128 x NT keys per workgroup), 'two-pass'
+    recomputes the region's logits (64-key tiles)."""
+    import torch
+
+    W, C, G, Hq = wl.window, wl.region, wl.n_q_heads // wl.n_kv_heads, wl.n_q_heads
+    rows = G * W
+    resident = (wl.dtype == torch.bfloat16 and wl.head_dim == 128 and W <= 2048 and rows <= 16384
+                and not flags & 1)
+    if not resident:
+        return "two-pass", W * (math.ceil(W / 64) * 64 + math.ceil(C / 64) * 64) * (Hq // G) * G
+
+    def keys(n):       # keys a launch with n resident keys multiplies: 8 waves x 16 NT, NT in {2, 4, 6, 8}
+        nt = -(-(-(-n // 8)) // 16)
+        nt = 2 if nt <= 2 else 4 if nt <= 4 else 6 if nt <= 6 else 8
+        return 8 * 16 * nt
+
+    rows_exec = (-(-rows // 16) + 1) * 16
+    if W <= 1024:
+        k = keys(W)
+    else:
+        k = keys(W - 1024) + 1024 + keys(max(C - 1024, 1))
+    return "resident", rows_exec * k * wl.n_kv_heads
 
 
 def read_traffic(workload):
@@ -62,7 +98,7 @@ def read_traffic(workload):
         return None
     with open(path) as f:
         d = json.load(f)
-    if d.get("source_sha256_16") != kernel_source_hash("kara_score_kernel.hpp"):
+    if d.get("source_sha256_16") != kernel_source_hash():
         return None
     return d.get("hbm_bytes_per_launch")
 
@@ -413,7 +449,8 @@ def run_batch(cfg, args, flags, steps, warmup, extras=True, keep_outputs=False):
     # one QK^T over the window: all W x W logits, or (unidirectional) the
     # W (W + 1) / 2 that causal attention needs
     score_flop = 2.0 * S * Lyr * Hq * (W * (W + 1) / 2 if uni else W * W) * D
-    exec_flop = 2.0 * S * Lyr * Hq * W * (math.ceil(W / 64) * 64 + math.ceil(C / 64) * 64) * D
+    path, exec_logits_sl = score_path(wl, flags)
+    exec_flop = 2.0 * S * Lyr * exec_logits_sl * D
     score_tflops = score_flop / (stage[0] / 1e3) / 1e12
     peak = PEAK_BF16_TFLOPS if wl.dtype == torch.bfloat16 else PEAK_FP32_MFMA_TFLOPS
     lens = ses.lens_h.tolist()
@@ -434,10 +471,14 @@ def run_batch(cfg, args, flags, steps, warmup, extras=True, keep_outputs=False):
                    "prefix_blocks": "materialised" if materialized else
                    "not materialised (table entries before the boundary block are never read by the step)",
                    "ablation": {0: "none", 1: "unidirectional", 2: "no_chunks", 3: "unidirectional+no_chunks"}[flags]},
-        "roofline": {"bound": "mfma", "kernel": "score_kernel", "achieved": round(score_tflops, 2),
+        "roofline": {"bound": "mfma",
+                     "kernel": ("score_resident_kernel" + (" (3 launches)" if W > 1024 else "")
+                                if path == "resident" else "score_kernel"),
+                     "achieved": round(score_tflops, 2),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(score_tflops / peak, 4),
                      "traffic": traffic, "algorithmic_flop_per_launch": score_flop,
-                     "executed_mfma_flop_per_launch": exec_flop if not uni else None},
+                     "executed_mfma_flop_per_launch": exec_flop if not uni else None,
+                     "scorer": path, "kernel_source_sha256_16": kernel_source_hash()},
         "stages_ms": {"score": round(stage[0], 4), "select": round(stage[1], 4),
                       "compact": round(stage[2], 4)},
         "kernel_ms_per_step": {"median": round(per_step[len(per_step) // 2], 4), "min": round(per_step[0], 4),

@@ -62,6 +62,7 @@ constexpr int kRRows = 16;                     // query rows per tile
 constexpr int kRKs = 4;                        // 32-wide reduction steps over D = 128
 constexpr int kRQStride = 272;                 // LDS bytes per staged query row (256 + pad)
 constexpr int kRQSlots = 4;                    // query tiles in the LDS ring
+constexpr int kZStride = kRWaves + 1;          // floats per row of the per-wave row sums
 
 enum Mode { kWhole = 0, kRowSums = 1, kWithRowSums = 2, kWeighted = 3 };
 
@@ -132,6 +133,10 @@ __global__ __launch_bounds__(kRThreads, 2) void score_resident_kernel(ScoreArgs 
 
   __shared__ __attribute__((aligned(16))) char qbuf[kRQSlots][kRRows * kRQStride];
   __shared__ __attribute__((aligned(16))) float zpart[2][kRWaves][kRRows];
+  // fast pass: per-wave row sums as [row][wave] with a row stride of 9 floats,
+  // so that neither the 16 writers of a wave nor the quads that read two
+  // waves' sums of one row meet in an LDS bank
+  __shared__ float zrs[2][kRRows * kZStride];
   __shared__ __attribute__((aligned(16))) float rowin[kRQSlots][kRRows];
   __shared__ float refs[kResidentMaxRows];
   __shared__ float zfull[kResidentMaxRows];
@@ -423,11 +428,11 @@ __global__ __launch_bounds__(kRThreads, 2) void score_resident_kernel(ScoreArgs 
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      float* zp = &zpart[t & 1][0][0];
+      float* zp = &zrs[t & 1][0];
       if (kRowSumsHere) {
         // this wave's sum of row 4 grp + (kl >> 2), published by one lane of each quad
         const float zw = row_sums16_transposed(rp, kl) - inval16;
-        if ((kl & 3) == 0) zp[wave * kRRows + 4 * grp + (kl >> 2)] = zw;
+        if ((kl & 3) == 0) zp[(4 * grp + (kl >> 2)) * kZStride + wave] = zw;
       }
       __syncthreads();
       float wm = 0.0f;
@@ -435,7 +440,7 @@ __global__ __launch_bounds__(kRThreads, 2) void score_resident_kernel(ScoreArgs 
         // the tile's normalisers: lane (grp, 4 m + q) adds waves 2q, 2q + 1 of row 4 grp + m
         const int m = 4 * grp + ((lane >> 2) & 3);
         const int q2 = 2 * (lane & 3);
-        const float za = zp[q2 * kRRows + m], zb = zp[(q2 + 1) * kRRows + m];
+        const float za = zp[m * kZStride + q2], zb = zp[m * kZStride + q2 + 1];
         const float zx = MODE == kWithRowSums ? rowin[t % kRQSlots][m] : 0.0f;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) nxt[nt] = mfma(qa[3], kf[nt][3], nxt[nt]);
