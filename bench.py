@@ -151,7 +151,8 @@ def cpu_baseline(wl, seqs, layers, flags=0, one_core=False, gpu=None):
     outputs for the same workload (`gpu`: host scores, candidates and kept
     sets of every unit), the sampled units' parity against this oracle run is
     counted: exact, near-tie accepted (tests/parity.py's rule at 1e-3) or
-    failed, and the largest relative score difference."""
+    failed, and the largest relative score difference; and every unit's
+    selection is replayed by the oracle in float32 on the GPU's own scores."""
     import numpy as np
     from threadpoolctl import threadpool_info, threadpool_limits
 
@@ -188,6 +189,8 @@ def cpu_baseline(wl, seqs, layers, flags=0, one_core=False, gpu=None):
                     v = adjudicate(s, wl.top_k, wl.budget, gpu["kept"][u], gpu["cand"][u], chunks=chunks)
                     counts["fail" if v.startswith("fail") else v] += 1
         out["parity"] = dict(counts, units=len(units) * Hkv, max_score_rel_err=worst)
+        if not one_core:
+            out["replay_all_units"] = replay_parity(wl, gpu, flags)
     return out
 
 
@@ -370,6 +373,8 @@ def run_trace(args, out_base):
     value = n_comp * W / (total_ms / 1e3)
     score_flop = 2.0 * n_comp * cfg.n_layers * cfg.n_q_heads * W * W * cfg.head_dim
     score_tflops = score_flop / (stage[0] / 1e3) / 1e12
+    # the trace's caches are bf16: the scorer is chosen by head size, window and rows
+    resident = cfg.head_dim == 128 and W <= 2048 and cfg.n_q_heads // cfg.n_kv_heads * W <= 16384
     log(f"{len(calls)} timed calls, {n_comp} sequence compressions, {total_ms:.1f} ms total")
     out = dict(out_base)
     out.update({
@@ -383,9 +388,12 @@ def run_trace(args, out_base):
                    "head_dim": cfg.head_dim, "window": W, "protect": cfg.protect, "top_k": cfg.top_k,
                    "budget": cfg.budget, "period": cfg.period, "lengths": f"{cfg.init_len}->{cfg.max_len}",
                    "events": tr.events, "compressions_timed": n_comp},
-        "roofline": {"bound": "mfma", "kernel": "score_kernel", "achieved": round(score_tflops, 2),
+        "roofline": {"bound": "mfma", "kernel": ("score_resident_kernel" if resident else "score_kernel"),
+                     "achieved": round(score_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(score_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "algorithmic_flop_total": score_flop},
+                     "traffic": None, "algorithmic_flop_total": score_flop,
+                     "scorer": "resident" if resident else "two-pass",
+                     "kernel_source_sha256_16": kernel_source_hash()},
         "stages_ms": {"score": round(stage[0], 3), "select": round(stage[1], 3), "compact": round(stage[2], 3)},
     })
     return out
@@ -593,7 +601,7 @@ def main():
             f"{out['cpu_baseline']['parity']}")
         out["cpu_baseline_1core"] = cpu_baseline(wl, seqs[:1], layers[:1], flags=args.flags, one_core=True)
         log(f"cpu baseline on one core {out['cpu_baseline_1core']['value']:.1f} window tokens/s")
-        out["parity"] = {"replay_all_units": replay_parity(wl, gpu, args.flags),
+        out["parity"] = {"replay_all_units": out["cpu_baseline"].pop("replay_all_units"),
                          "sampled_vs_float64_oracle": out["cpu_baseline"]["parity"],
                          "rule": "scores within 1e-3 relative; selection replayed in float32 on the GPU's scores "
                                  "bit-exact for every unit; sampled units exact or near-ties within 1e-3"}

@@ -74,8 +74,11 @@ def test_static_scratch_rejects_oversized_calls():
     print("[case] static scratch: oversized call rejected", flush=True)
     wl = synth.make_workload(2, device="cuda", n_seqs=2, n_layers=1)
     ses = runner.Session(wl)
-    # a batch whose scratch need exceeds the array: the lengths tensor sets n_seqs
-    n = int(kara.kara_static_scratch_bytes() // kara.kara_workspace_bytes(ses.shape, ses.params, 1)) + 8
+    # a batch whose scratch need exceeds the array (the lengths tensor sets
+    # n_seqs; the workspace's segments are padded, so the need is not linear in n)
+    n = 1
+    while kara.kara_workspace_bytes(ses.shape, ses.params, n) <= kara.kara_static_scratch_bytes():
+        n *= 2
     lens_h = torch.full((n,), int(ses.lens_h[0]), dtype=torch.int32)
     table_h = ses.table_h[:1].repeat(n, 1).contiguous()
     pool = ses.new_pool()
