@@ -36,8 +36,11 @@
 // [2^-40, 2^100] (logits beyond about +-27 / 69 nats) sends the unit to an
 // exact route that first takes every row's maximum over all keys, then the
 // normalisers with those references, then the column sums (slow, key block by
-// key block; never taken on ordinary data).  For two-block windows the check
-// is made by kWithRowSums and the exact route run by kWeighted.
+// key block; never taken on ordinary data).  For one-block windows kWhole
+// marks such a unit (a negative first score) and a second, grid-stride launch
+// runs the route for the marked units only, so that the route's code does not
+// share the main kernel's register budget; for two-block windows the check is
+// made by kWithRowSums and the route run by kWeighted.
 //
 // Registers (two waves per SIMD, at most 256 each): 4 NT x 4 for the keys,
 // 2 x 4 NT for two logit tiles (the next tile's MFMAs run while the VALU works
@@ -62,9 +65,11 @@ constexpr int kRRows = 16;                     // query rows per tile
 constexpr int kRKs = 4;                        // 32-wide reduction steps over D = 128
 constexpr int kRQStride = 272;                 // LDS bytes per staged query row (256 + pad)
 constexpr int kRQSlots = 4;                    // query tiles in the LDS ring
+constexpr int kRRowSlots = 8;                  // tiles of staged per-row inputs in LDS
 constexpr int kZStride = kRWaves + 1;          // floats per row of the per-wave row sums
+constexpr int kExactGrid = 512;                // workgroups of the exact launch (grid-stride)
 
-enum Mode { kWhole = 0, kRowSums = 1, kWithRowSums = 2, kWeighted = 3 };
+enum Mode { kWhole = 0, kRowSums = 1, kWithRowSums = 2, kWeighted = 3, kExact = 4 };
 
 template <int kCtrl>
 __device__ __forceinline__ float dpp(float x) {
@@ -124,26 +129,36 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// LDS of one workgroup.
+struct ResidentLds {
+  __attribute__((aligned(16))) char qbuf[kRQSlots][kRRows * kRQStride];
+  __attribute__((aligned(16))) float zpart[2][kRWaves][kRRows];
+  // fast pass: per-wave row sums as [row][wave] with a row stride of 9 floats,
+  // so that neither the 16 writers of a wave nor the quads that read two
+  // waves' sums of one row meet in an LDS bank
+  float zrs[2][kRRows * kZStride];
+  __attribute__((aligned(16))) float rowin[kRRowSlots][kRRows];
+  float refs[kResidentMaxRows];
+  float zfull[kResidentMaxRows];
+  int s_redo;
+};
+
+// One unit's scores on one workgroup.  MODE kExact runs the exact route only
+// (for a unit that the kWhole launch marked).
 template <int NT, int MODE>
-__global__ __launch_bounds__(kRThreads, 2) void score_resident_kernel(ScoreArgs a) {
+__device__ __forceinline__ void score_unit(const ScoreArgs& a, const int unit, ResidentLds& sm) {
   constexpr bool kRowSumsHere = MODE != kWeighted;     // this launch computes row normalisers
   constexpr bool kCols = MODE != kRowSums;              // this launch adds column sums
   constexpr bool kStageRow = MODE == kWithRowSums || MODE == kWeighted;   // a per-row input is staged
   constexpr int kBlockKeys = kRWaves * 16 * NT;
+  auto& qbuf = sm.qbuf;
+  auto& zpart = sm.zpart;
+  auto& zrs = sm.zrs;
+  auto& rowin = sm.rowin;
+  auto& refs = sm.refs;
+  auto& zfull = sm.zfull;
+  auto& s_redo = sm.s_redo;
 
-  __shared__ __attribute__((aligned(16))) char qbuf[kRQSlots][kRRows * kRQStride];
-  __shared__ __attribute__((aligned(16))) float zpart[2][kRWaves][kRRows];
-  // fast pass: per-wave row sums as [row][wave] with a row stride of 9 floats,
-  // so that neither the 16 writers of a wave nor the quads that read two
-  // waves' sums of one row meet in an LDS bank
-  __shared__ float zrs[2][kRRows * kZStride];
-  __shared__ __attribute__((aligned(16))) float rowin[kRQSlots][kRRows];
-  __shared__ float refs[kResidentMaxRows];
-  __shared__ float zfull[kResidentMaxRows];
-  __shared__ int s_redo;
-
-  const int unit = blockIdx.x;
-  if (unit >= a.n_units) return;
   const int h = unit % a.Hkv;
   const int bl = unit / a.Hkv;
   const int l = bl % a.Lyr;
@@ -217,13 +232,16 @@ __global__ __launch_bounds__(kRThreads, 2) void score_resident_kernel(ScoreArgs 
   const int st_off = (tid & 31) * 8;
   const int di = kRRows / G, dg = kRRows - (kRRows / G) * G;
   int ld_i = st_row / G, ld_g = st_row - (st_row / G) * G, ld_row = st_row;
-  // loads the thread's piece of the next tile in sequence (tiles 0, 1, 2, ...)
+  // Loads the thread's piece of the next tile in sequence (tiles 0, 1, 2, ...).
+  // The load is unconditional, so that the compiler can wait for each piece by
+  // count rather than for every load in flight: rows past the last one read
+  // the last row again (finite values; their normaliser weights are zero).
+  // Offsets within the unit's window fit 32 bits (W * Hq * 256 bytes).
   auto load_q = [&]() -> uint2 {
-    uint2 v = make_uint2(0u, 0u);
-    if (ld_row < rows) {
-      const int slot_i = ld_i + ring_off < W ? ld_i + ring_off : ld_i + ring_off - W;
-      v = *(const uint2*)(qbase + ((size_t)slot_i * a.Hq + ld_g) * 256 + st_off);
-    }
+    const bool ok = ld_row < rows;
+    const int i = ok ? ld_i : W - 1, g = ok ? ld_g : G - 1;
+    const int slot_i = i + ring_off < W ? i + ring_off : i + ring_off - W;
+    const uint2 v = *(const uint2*)(qbase + ((uint32_t)(slot_i * a.Hq + g) * 256u + (uint32_t)st_off));
     ld_row += kRRows;
     ld_i += di;
     ld_g += dg;
@@ -246,14 +264,17 @@ __global__ __launch_bounds__(kRThreads, 2) void score_resident_kernel(ScoreArgs 
     return *(const bf16x8*)&qbuf[t % kRQSlots][kl * kRQStride + ks * 64 + grp * 16];
   };
   // Per-row input of tile t (kWithRowSums: the partial normaliser over KB1;
-  // kWeighted: 1 / Z), staged through LDS like the query tiles by threads
-  // 0..15 (0 for rows past the last one).
+  // kWeighted: 1 / Z), staged through LDS like the query tiles and stored by
+  // threads 0..15 (0 for rows past the last one).  The load is unconditional
+  // for the same reason as the query pieces' (every wave reads row
+  // t * 16 + (tid & 15), clamped to the last row).
   auto load_row = [&](int t) -> float {
-    const int row = t * kRRows + tid;
-    return (kStageRow && tid < kRRows && row < rows) ? zrow[row] : 0.0f;
+    if (!kStageRow) return 0.0f;
+    const int row = t * kRRows + (tid & (kRRows - 1));
+    return zrow[row < rows ? row : rows - 1];
   };
   auto store_row = [&](float v, int t) {
-    if (kStageRow && tid < kRRows) rowin[t % kRQSlots][tid] = v;
+    if (kStageRow && tid < kRRows) rowin[t % kRRowSlots][tid] = t * kRRows + tid < rows ? v : 0.0f;
   };
   // 16 x (16 NT) logits of tile t: row 4 grp + r, key (block key) 16 NT wave + 16 nt + kl
   auto tile_mfma = [&](f32x4 (&acc)[NT], int t) {
@@ -360,6 +381,10 @@ __global__ __launch_bounds__(kRThreads, 2) void score_resident_kernel(ScoreArgs 
     }
   };
 
+  if (MODE == kExact) {
+    exact_unit();
+    return;
+  }
   if (tid == 0) s_redo = 0;
 
   // kWeighted: a unit whose normalisers left float's comfortable range in
@@ -374,7 +399,6 @@ __global__ __launch_bounds__(kRThreads, 2) void score_resident_kernel(ScoreArgs 
   const float n_inval = load_keys(key_lo, key_hi);
   // keys past the block among the 16 lanes of the row group (logit 0, exp2 = 1)
   const float inval16 = row_sum16(n_inval);
-  const bool col_wave = kCols && key_lo + wave * 16 * NT < C;   // the wave holds region keys
   float colacc[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) colacc[nt] = 0.0f;
@@ -390,14 +414,25 @@ __global__ __launch_bounds__(kRThreads, 2) void score_resident_kernel(ScoreArgs 
     __syncthreads();
     f32x4 acc0[NT], acc1[NT];
     tile_mfma(acc0, 0);
-    // One tile: `cur` holds its logits, the next tile's go into `nxt`; `stg`
-    // and `sr` carry tile t + 2's query piece and row input to their LDS
-    // slots and then fetch tile t + 4's.
-    auto step = [&](f32x4 (&cur)[NT], f32x4 (&nxt)[NT], uint2& stg, float& sr, int t) {
-      store_q(stg, t + 2);
-      stg = load_q();
-      store_row(sr, t + 2);
-      sr = load_row(t + 4);
+    // One tile: `cur` holds its logits, the next tile's go into `nxt`.  The
+    // first step of each pair (t even) stores tiles t + 2 and t + 3 (query
+    // pieces and row inputs loaded two steps earlier) to their LDS slots and
+    // fetches tiles t + 4 and t + 5, so that the loads in flight when a pair
+    // starts are a whole pair old.  The query slot of tile t + 3 last held
+    // tile t - 1, whose fragments were read before the previous step's
+    // barrier; the row inputs keep eight slots because a tile's are read after
+    // its barrier.
+    auto step = [&](f32x4 (&cur)[NT], f32x4 (&nxt)[NT], int t, bool stage) {
+      if (stage) {
+        store_q(stg0, t + 2);
+        store_q(stg1, t + 3);
+        store_row(sr0, t + 2);
+        store_row(sr1, t + 3);
+        stg0 = load_q();
+        stg1 = load_q();
+        sr0 = load_row(t + 4);
+        sr1 = load_row(t + 5);
+      }
       // The next tile's logits (past the last tile: zero rows, never used) on
       // the matrix cores while this tile's VALU work runs, in regions fenced
       // against reordering: one region per logit of the lane (its multiply,
@@ -405,12 +440,16 @@ __global__ __launch_bounds__(kRThreads, 2) void score_resident_kernel(ScoreArgs 
       // 0-2; consecutive ones update different N-tiles); the last step's
       // MFMAs are issued while the normalisers' LDS reads are in flight.  A
       // wave thus issues VALU work while its own MFMAs execute.
-      bf16x8 qa[kRKs];
+      // query fragments of the next tile: steps 0-2 now, step 3 after the barrier
+      bf16x8 qa[kRKs - 1];
 #pragma unroll
-      for (int ks = 0; ks < kRKs; ++ks) qa[ks] = qfrag(t + 1, ks);
+      for (int ks = 0; ks < kRKs - 1; ++ks) qa[ks] = qfrag(t + 1, ks);
       float rp[4];
+      // region k: the multiply of the lane's logit k, the exp2 of logit k - 1
+      // and the row-sum add of logit k - 2 (no operation waits on the one
+      // before it in its region), in place in `cur`
 #pragma unroll
-      for (int k = 0; k < 4 * NT; ++k) {
+      for (int k = 0; k < 4 * NT + 2; ++k) {
         if (k < 3 * NT) {
           const int ks = k / NT, nt = k % NT;
           if (ks == 0) {
@@ -420,11 +459,14 @@ __global__ __launch_bounds__(kRThreads, 2) void score_resident_kernel(ScoreArgs 
             nxt[nt] = mfma(qa[ks], kf[nt][ks], nxt[nt]);
           }
         }
-        {
-          const int nt = k / 4, r = k % 4;
-          const float x = __builtin_amdgcn_exp2f(cur[nt][r] * c);
-          cur[nt][r] = x;
-          if (kRowSumsHere) rp[r] = nt == 0 ? x : rp[r] + x;
+        if (k < 4 * NT) cur[k / 4][k % 4] *= c;
+        if (k >= 1 && k <= 4 * NT) {
+          const int j = k - 1;
+          cur[j / 4][j % 4] = __builtin_amdgcn_exp2f(cur[j / 4][j % 4]);
+        }
+        if (kRowSumsHere && k >= 2) {
+          const int j = k - 2, nt = j / 4, r = j % 4;
+          rp[r] = nt == 0 ? cur[nt][r] : rp[r] + cur[nt][r];
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -435,57 +477,65 @@ __global__ __launch_bounds__(kRThreads, 2) void score_resident_kernel(ScoreArgs 
         if ((kl & 3) == 0) zp[(4 * grp + (kl >> 2)) * kZStride + wave] = zw;
       }
       __syncthreads();
-      float wm = 0.0f;
+      // The tile's normalisers from LDS: lane (grp, 4 m + q) adds waves 2q,
+      // 2q + 1 of row 4 grp + m.  Half of the last reduction step's MFMAs are
+      // issued while those reads are in flight, the other half between the
+      // column sums' FMAs.
+      const int m = 4 * grp + ((lane >> 2) & 3);
+      const int q2 = 2 * (lane & 3);
+      const bf16x8 q3 = qfrag(t + 1, kRKs - 1);
+      float za = 0.0f, zb = 0.0f, zx = 0.0f;
+      float4 wrow = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
       if (kRowSumsHere) {
-        // the tile's normalisers: lane (grp, 4 m + q) adds waves 2q, 2q + 1 of row 4 grp + m
-        const int m = 4 * grp + ((lane >> 2) & 3);
-        const int q2 = 2 * (lane & 3);
-        const float za = zp[m * kZStride + q2], zb = zp[m * kZStride + q2 + 1];
-        const float zx = MODE == kWithRowSums ? rowin[t % kRQSlots][m] : 0.0f;
+        za = zp[m * kZStride + q2];
+        zb = zp[m * kZStride + q2 + 1];
+        if (MODE == kWithRowSums) zx = rowin[t % kRRowSlots][m];
+      } else {
+        wrow = *(const float4*)&rowin[t % kRRowSlots][4 * grp];
+      }
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) nxt[nt] = mfma(qa[3], kf[nt][3], nxt[nt]);
-        __builtin_amdgcn_sched_barrier(0);
+      for (int nt = 0; nt < NT / 2; ++nt) nxt[nt] = mfma(q3, kf[nt][3], nxt[nt]);
+      __builtin_amdgcn_sched_barrier(0);
+      float w0 = wrow.x, w1 = wrow.y, w2 = wrow.z, w3 = wrow.w;
+      if (kRowSumsHere) {
         const float z = quad_sum(za + zb) + zx;
         const bool row_ok = t * kRRows + m < rows;
         if (MODE != kRowSums) bad |= __ballot(row_ok && !(z >= 0x1p-40f && z <= 0x1p100f)) != 0;
         if (MODE == kRowSums) {
           if (wave == 0 && (lane & 3) == 0 && row_ok) zrow[t * kRRows + m] = z;
         } else {
-          wm = row_ok ? __builtin_amdgcn_rcpf(z) : 0.0f;
+          const float wm = row_ok ? __builtin_amdgcn_rcpf(z) : 0.0f;
           if (MODE == kWithRowSums && wave == 0 && (lane & 3) == 0 && row_ok) zrow[t * kRRows + m] = wm;
-        }
-      } else {
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) nxt[nt] = mfma(qa[3], kf[nt][3], nxt[nt]);
-      }
-      if (kCols && col_wave) {
-        float w0, w1, w2, w3;
-        if (kRowSumsHere) {
           w0 = row_bcast<0>(wm);
           w1 = row_bcast<1>(wm);
           w2 = row_bcast<2>(wm);
           w3 = row_bcast<3>(wm);
-        } else {
-          const float4 w = *(const float4*)&rowin[t % kRQSlots][4 * grp];
-          w0 = w.x;
-          w1 = w.y;
-          w2 = w.z;
-          w3 = w.w;
         }
+      }
+      // column sums (every wave adds them, so that all waves reach the next
+      // barrier together; only region keys are written)
+      auto cols = [&](int nt) {
+        float s = colacc[nt];
+        s = fmaf(cur[nt][0], w0, s);
+        s = fmaf(cur[nt][1], w1, s);
+        s = fmaf(cur[nt][2], w2, s);
+        s = fmaf(cur[nt][3], w3, s);
+        colacc[nt] = s;
+      };
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          float s = colacc[nt];
-          s = fmaf(cur[nt][0], w0, s);
-          s = fmaf(cur[nt][1], w1, s);
-          s = fmaf(cur[nt][2], w2, s);
-          s = fmaf(cur[nt][3], w3, s);
-          colacc[nt] = s;
-        }
+      for (int nt = 0; nt < NT / 2; ++nt) {
+        nxt[NT / 2 + nt] = mfma(q3, kf[NT / 2 + nt][3], nxt[NT / 2 + nt]);
+        if (kCols) cols(nt);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (kCols) {
+#pragma unroll
+        for (int nt = NT / 2; nt < NT; ++nt) cols(nt);
       }
     };
     for (int t = 0; t < n_tiles; t += 2) {
-      step(acc0, acc1, stg0, sr0, t);
-      if (t + 1 < n_tiles) step(acc1, acc0, stg1, sr1, t + 1);
+      step(acc0, acc1, t, true);
+      if (t + 1 < n_tiles) step(acc1, acc0, t + 1, false);
     }
   }
 
@@ -499,10 +549,45 @@ __global__ __launch_bounds__(kRThreads, 2) void score_resident_kernel(ScoreArgs 
     return;
   }
   if (MODE == kWhole && s_redo) {       // uniform over the workgroup
-    exact_unit();
+    // marked for the exact launch: scores are never negative, and that
+    // launch overwrites every score of the unit
+    if (tid == 0) out[0] = -1.0f;
     return;
   }
   write_cols(colacc, key_lo, key_hi);
+}
+
+template <int NT, int MODE>
+__global__ __launch_bounds__(kRThreads, 2) void score_resident_kernel(ScoreArgs a) {
+  __shared__ ResidentLds sm;
+  if ((int)blockIdx.x >= a.n_units) return;
+  score_unit<NT, MODE>(a, blockIdx.x, sm);
+}
+
+// The exact route for the units of a one-launch window that the kWhole launch
+// marked (first score negative).  A grid-stride pass: each workgroup checks
+// the marks of units blockIdx.x + gridDim.x * (tid + kRThreads * r) and
+// scores the marked ones one after another.  Kept apart from kWhole so that
+// the route's code does not share that kernel's register budget.
+template <int NT>
+__global__ __launch_bounds__(kRThreads, 2) void exact_resident_kernel(ScoreArgs a) {
+  __shared__ ResidentLds sm;
+  __shared__ int s_list[kRThreads];
+  __shared__ int s_n;
+  const int stride = (int)gridDim.x * kRThreads;
+  for (int u0 = blockIdx.x; u0 < a.n_units; u0 += stride) {
+    const long u = (long)u0 + (long)threadIdx.x * gridDim.x;
+    const bool marked = u < a.n_units && a.out[u * a.C] < 0.0f;
+    if (threadIdx.x == 0) s_n = 0;
+    __syncthreads();
+    if (marked) s_list[atomicAdd(&s_n, 1)] = (int)u;
+    __syncthreads();
+    const int n = s_n;
+    for (int i = 0; i < n; ++i) {
+      score_unit<NT, kExact>(a, s_list[i], sm);
+      __syncthreads();
+    }
+  }
 }
 
 template <int NT, int MODE>
@@ -534,7 +619,16 @@ int resident_tiles(int n_keys) {
 
 hipError_t launch_score_resident(const ScoreArgs& a, hipStream_t stream) {
   if (a.n_units == 0) return hipSuccess;
-  if (a.W <= kResidentBlock) return launch_mode<kWhole>(a, 0, a.W, stream);
+  if (a.W <= kResidentBlock) {
+    hipError_t e = launch_mode<kWhole>(a, 0, a.W, stream);
+    if (e != hipSuccess) return e;
+    ScoreArgs b = a;
+    b.key_lo = 0;
+    b.key_hi = a.W;
+    const unsigned grid = (unsigned)(a.n_units < kExactGrid ? a.n_units : kExactGrid);
+    hipLaunchKernelGGL((exact_resident_kernel<8>), dim3(grid), dim3(kRThreads), 0, stream, b);
+    return hipGetLastError();
+  }
   if (!a.zrow || !a.uflags) return hipErrorInvalidValue;
   hipError_t e;
   if ((e = launch_mode<kRowSums>(a, kResidentBlock, a.W, stream)) != hipSuccess) return e;
