@@ -525,7 +525,8 @@ kara_status kara_append(const kara_shape* shape, int32_t window, int32_t n_seqs,
 
 size_t kara_attention_workspace_bytes(const kara_shape* shape, int32_t n_seqs, int32_t max_len) {
   if (check_shape(shape) != KARA_OK || n_seqs < 0 || max_len < 1) return 0;
-  const size_t n_split = (size_t)ceil_div(max_len, kara::kAttnChunk);
+  // sized for the finer split, whichever the launch picks
+  const size_t n_split = (size_t)ceil_div(max_len, kara::kAttnChunkMin);
   const size_t parts = (size_t)n_seqs * shape->n_q_heads * n_split;
   return align_up(parts * shape->head_dim * sizeof(float)) + align_up(parts * 2 * sizeof(float));
 }
@@ -544,6 +545,10 @@ kara_status kara_decode_attention(const kara_shape* shape, int32_t n_seqs, int32
   if (layer < 0 || layer >= shape->n_layers)
     return fail(KARA_E_INVAL, "layer %d outside [0, %d)", layer, shape->n_layers);
   if (n_blocks < 1 || max_blocks < 1) return fail(KARA_E_INVAL, "n_blocks and max_blocks must be >= 1");
+  // the kernel indexes a layer's K rows with 32-bit row numbers
+  if ((uint64_t)n_blocks * shape->n_kv_heads * shape->block_size >= ((uint64_t)1 << 32))
+    return fail(KARA_E_UNSUPPORTED, "n_blocks * n_kv_heads * block_size = %llu rows per layer exceed 2^32",
+                (unsigned long long)n_blocks * shape->n_kv_heads * shape->block_size);
   if (n_seqs == 0) return KARA_OK;
   if (!seq_lens_h) return fail(KARA_E_INVAL, "host lengths NULL");
   int32_t max_len = 0;
@@ -571,9 +576,15 @@ kara_status kara_decode_attention(const kara_shape* shape, int32_t n_seqs, int32
   a.Hkv = shape->n_kv_heads;
   a.D = shape->head_dim;
   a.bs = shape->block_size;
+  a.bs_shift = log2_exact(shape->block_size);
   a.NB = n_blocks;
   a.MB = max_blocks;
-  a.n_split = ceil_div(max_len, kara::kAttnChunk);
+  // 1024-token splits when they alone give the launch enough workgroups
+  long big_grid = 0;
+  for (int32_t b = 0; b < n_seqs; ++b) big_grid += ceil_div(seq_lens_h[b], kara::kAttnChunkMax);
+  big_grid *= shape->n_kv_heads;
+  a.chunk = big_grid >= kara::kAttnBigGrid ? kara::kAttnChunkMax : kara::kAttnChunkMin;
+  a.n_split = ceil_div(max_len, a.chunk);
   a.c = (float)(1.4426950408889634 / std::sqrt((double)shape->head_dim));
   const size_t parts = (size_t)n_seqs * a.Hq * a.n_split;
   a.part_o = (float*)workspace;

@@ -12,17 +12,18 @@
 //   the compressed cache is served through PagedAttention).  It is bound by
 //   HBM: per token and KV head it reads one K and one V row (2 * D * elt
 //   bytes) and does 4 * G * D flops.  Layout of the work:
-//     * a workgroup takes 512 tokens of one (sequence, KV head) ("split");
+//     * a workgroup takes 512 or 1024 tokens of one (sequence, KV head)
+//       ("split"; the host picks 1024 for launches with many workgroups);
 //       the G query heads of the group share every K/V row it reads, and the
-//       split's block ids are staged in LDS first;
-//     * 16 lanes hold one token's row as 16-byte pieces, so a wave loads 4
-//       tokens' rows per instruction, fully coalesced within a block row;
-//     * each lane group takes 4 tokens per step (8 loads in flight per lane);
-//       bf16 dot products use the packed bf16 dot instruction (two products
-//       per instruction, no unpacking of K) and are summed across the 16
-//       lanes with DPP row permutations;
+//       split's block ids (loaded in the same round trip as the sequence's
+//       length) are staged in LDS as row indices; splits past the sequence's
+//       end exit at once;
+//     * bf16: QK^T of 16 tokens per wave step on the matrix cores (see
+//       attention_mfma_kernel); float32: D / 4 lanes hold one token's row as
+//       16-byte pieces and dot products are summed across those lanes with
+//       DPP row permutations (attention_kernel);
 //     * a running maximum, sum and output per query head are rescaled only
-//       when some lane's maximum moves;
+//       when a maximum moves;
 //     * lane groups, waves and then splits are merged with the usual
 //       (max, sum, output) rescaling; the split merge is a second kernel.
 //   Logits are kept in log2 units (the dot products are scaled by
@@ -150,7 +151,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
   constexpr bool kBf16 = sizeof(T) == 2;
   __shared__ float sh_m[kAttnWaves][G], sh_l[kAttnWaves][G];
   __shared__ float sh_o[kAttnWaves][G][D];
-  __shared__ int32_t sh_blk[kAttnChunk + 1];
+  __shared__ int32_t sh_blk[kAttnChunkMax + 1];
 
   const int split = blockIdx.x % a.n_split;
   const int h = (blockIdx.x / a.n_split) % a.Hkv;
@@ -161,8 +162,11 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
   int L = a.lens[b];
   const int max_tok = a.MB * a.bs;
   L = L < 1 ? 1 : (L > max_tok ? max_tok : L);
-  const int t0 = split * kAttnChunk;
-  const int t1 = min(L, t0 + kAttnChunk);
+  const int t0 = split * a.chunk;
+  // splits past the sequence's end hold nothing; the combine reads only the
+  // sequence's own splits (same clamped length)
+  if (t0 >= L) return;
+  const int t1 = min(L, t0 + a.chunk);
 
   // the split's block ids, clamped to the pool
   const int e0 = t0 / a.bs;
@@ -304,6 +308,245 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
   }
 }
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp_max(float x) {
+  return fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, 0xF,
+                                                                        0xF, false)));
+}
+
+// Maximum / sum over the 16 lanes of a DPP row.
+__device__ __forceinline__ float row_max16(float x) {
+  x = dpp_max<0xB1>(x);     // quad_perm [1,0,3,2]
+  x = dpp_max<0x4E>(x);     // quad_perm [2,3,0,1]
+  x = dpp_max<0x141>(x);    // row_half_mirror
+  return dpp_max<0x140>(x); // row_mirror
+}
+
+// bf16 decode attention with QK^T on the matrix cores.  Per step a wave takes
+// 16 consecutive tokens of the split: v_mfma_f32_16x16x32_bf16 multiplies the
+// group's query heads (A operand: head = lane & 15, zero rows past G) by the
+// 16 tokens' keys (B operand, loaded straight from the cache rows: token =
+// lane & 15, dims 32 ks + 8 (lane >> 4) .. + 7), giving lane l the logits of
+// heads 4 (l >> 4) .. + 3 for token l & 15.  The running maximum of a head is
+// then one value per 16-lane row (a DPP row maximum), so every lane of the
+// wave shares it; each lane keeps the partial sum of its own token column.
+// P times V stays in float32 FMAs: the probabilities go through the wave's
+// LDS tile [token][head] to the V layout (D / 8 lanes per 16-byte-piece row,
+// 64 / (D / 8) rows per wave-wide load), and since the maximum is common to
+// the wave, the lane groups' outputs are added without rescaling at the end.
+template <int D, int G>
+__global__ __launch_bounds__(kAttnThreads) void attention_mfma_kernel(AttnArgs a) {
+  static_assert(G >= 1 && G <= 8, "query heads per KV head");
+  constexpr int kKs = D / 32;               // reduction steps of 32 dims
+  constexpr int kLanes = D / 8;             // lanes per V row (16-byte pieces)
+  constexpr int kGroups = 64 / kLanes;      // V rows per wave-wide load
+  constexpr int kT = 16;                    // tokens per wave step
+  constexpr int kV = kT / kGroups;          // V rows per lane per step
+  constexpr int kRowBytes = D * 2;
+  constexpr int kRG = (G + 3) / 4;          // 16-lane rows holding query heads
+  __shared__ float sh_m[kAttnWaves][G], sh_l[kAttnWaves][G];
+  __shared__ float sh_o[kAttnWaves][G][D];
+  __shared__ int32_t sh_blk[kAttnChunkMax + 1];
+  __shared__ __attribute__((aligned(16))) float sh_p[kAttnWaves][kT][8];
+
+  const int split = blockIdx.x % a.n_split;
+  const int h = (blockIdx.x / a.n_split) % a.Hkv;
+  const int b = blockIdx.x / (a.n_split * a.Hkv);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  // The split's blocks as the index of their first K row of head h within
+  // the layer (rows of kRowBytes; fits 32 bits: the layer's K rows are
+  // NB Hkv bs), block ids clamped to the pool.  The table entries of the
+  // whole chunk (within the table row) are loaded together with the length,
+  // so that the two loads take one round trip.
+  const int t0 = split * a.chunk;
+  const int e0 = t0 >> a.bs_shift;
+  const int n_chunk = min(((a.chunk - 1) >> a.bs_shift) + 1, a.MB - e0);
+  int blk_pre[(kAttnChunkMax + kAttnThreads - 1) / kAttnThreads];
+#pragma unroll
+  for (int k = 0; k < (kAttnChunkMax + kAttnThreads - 1) / kAttnThreads; ++k) {
+    const int i = tid + k * kAttnThreads;
+    blk_pre[k] = i < n_chunk ? a.table[(size_t)b * a.MB + e0 + i] : 0;
+  }
+  int L = a.lens[b];
+  const int max_tok = a.MB * a.bs;
+  L = L < 1 ? 1 : (L > max_tok ? max_tok : L);
+  // splits past the sequence's end hold nothing; the combine reads only the
+  // sequence's own splits (same clamped length)
+  if (t0 >= L) return;
+  const int t1 = min(L, t0 + a.chunk);
+  const int n_e = ((t1 - 1) >> a.bs_shift) - e0 + 1;
+#pragma unroll
+  for (int k = 0; k < (kAttnChunkMax + kAttnThreads - 1) / kAttnThreads; ++k) {
+    const int i = tid + k * kAttnThreads;
+    if (i < n_e) {
+      const int blk = blk_pre[k] < 0 ? 0 : (blk_pre[k] >= a.NB ? a.NB - 1 : blk_pre[k]);
+      sh_blk[i] = (int32_t)(((uint32_t)blk * (uint32_t)a.Hkv + (uint32_t)h) << a.bs_shift);
+    }
+  }
+  // query heads as the A operand (rows past G are zero)
+  const int col = lane & 15, rg = lane >> 4;
+  bf16x8 qa[kKs];
+#pragma unroll
+  for (int ks = 0; ks < kKs; ++ks) {
+    if (col < G) {
+      qa[ks] = *(const bf16x8*)((const char*)a.q + (((size_t)b * a.Hq + h * G + col) * D + 32 * ks + 8 * rg) * 2);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qa[ks][e] = (__bf16)0.0f;
+    }
+  }
+  __syncthreads();
+
+  float mrun[4], lrun[4];                   // heads 4 rg + r: running maximum (log2), sum over this lane's tokens
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    mrun[r] = -INFINITY;
+    lrun[r] = 0.0f;
+  }
+  const int vsub = lane % kLanes, vgrp = lane / kLanes;
+  float o[G][8];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[g][e] = 0.0f;
+
+  const char* kbase = (const char*)a.pool + (size_t)a.layer * 2 * a.NB * a.Hkv * a.bs * kRowBytes;
+  const char* vbase = kbase + (size_t)a.NB * a.Hkv * a.bs * kRowBytes;
+  const int bs_mask = a.bs - 1;
+  // K or V row of token t (t inside the split)
+  auto row_ptr = [&](const char* base, int t) -> const char* {
+    const uint32_t row = (uint32_t)sh_blk[(t >> a.bs_shift) - e0] + (uint32_t)(t & bs_mask);
+    return base + (size_t)row * kRowBytes;
+  };
+  float* pt = &sh_p[wave][0][0];
+
+  for (int base = t0 + wave * kT; base < t1; base += kAttnWaves * kT) {
+    // keys of token base + col (clamped; masked below) and this lane's V rows
+    const char* kp = row_ptr(kbase, min(base + col, t1 - 1)) + 16 * rg;
+    u32x4 kw[kKs];
+#pragma unroll
+    for (int ks = 0; ks < kKs; ++ks) kw[ks] = __builtin_nontemporal_load((const u32x4*)(kp + 64 * ks));
+    u32x4 vw[kV];
+#pragma unroll
+    for (int j = 0; j < kV; ++j)
+      vw[j] = __builtin_nontemporal_load(
+          (const u32x4*)(row_ptr(vbase, min(base + vgrp + kGroups * j, t1 - 1)) + 16 * vsub));
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int ks = 0; ks < kKs; ++ks) {
+      bf16x8 kf;
+      __builtin_memcpy(&kf, &kw[ks], 16);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], kf, acc, 0, 0, 0);
+    }
+    const bool tok_ok = base + col < t1;
+    float x[4], mx[4];
+    bool moved = false;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      x[r] = tok_ok ? acc[r] * a.c : -INFINITY;
+      mx[r] = fmaxf(mrun[r], row_max16(x[r]));
+      moved |= 4 * rg + r < G && mx[r] > mrun[r];
+    }
+    // a head's maximum moved (rare after the first steps): rescale its sums
+    // and outputs (the factor of head g is held by lane 16 (g / 4))
+    if (__ballot(moved)) {
+      float sc[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sc[r] = mx[r] == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(mrun[r] - mx[r]);
+        lrun[r] *= sc[r];
+        mrun[r] = mx[r];
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float s = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sc[g % 4]), 16 * (g / 4)));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[g][e] *= s;
+      }
+    }
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      p[r] = x[r] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(x[r] - mrun[r]);
+      lrun[r] += p[r];
+    }
+    // probabilities to the V layout through the wave's tile [token][head]
+    if (rg < kRG) *(float4*)&pt[col * 8 + 4 * rg] = make_float4(p[0], p[1], p[2], p[3]);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int j = 0; j < kV; ++j) {
+      const int tl = vgrp + kGroups * j;
+      float pv[8];
+      *(float4*)&pv[0] = *(const float4*)&pt[tl * 8];
+      if (G > 4) *(float4*)&pv[4] = *(const float4*)&pt[tl * 8 + 4];
+      float vf[8];
+      unpack<__bf16>(vw[j], vf);
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[g][e] = fmaf(pv[g], vf[e], o[g][e]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+
+  // the wave's sums over its 16 token columns, and its outputs over the lane
+  // groups (same dims, different tokens, one running maximum per head)
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    float v = lrun[r];
+    v = dpp_add<0xB1>(v);
+    v = dpp_add<0x4E>(v);
+    v = dpp_add<0x141>(v);
+    lrun[r] = dpp_add<0x140>(v);
+  }
+#pragma unroll
+  for (int off = kLanes; off < 64; off <<= 1)
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[g][e] += __shfl_xor(o[g][e], off);
+  if (col == 0 && rg < kRG) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int g = 4 * rg + r;
+      if (g < G) {
+        sh_m[wave][g] = mrun[r];
+        sh_l[wave][g] = lrun[r];
+      }
+    }
+  }
+  if (vgrp == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sh_o[wave][g][vsub * 8 + e] = o[g][e];
+  }
+  __syncthreads();
+  // merge the waves and write this split's (max, sum, output) per query head
+  const size_t part = (size_t)(b * a.Hq + h * G) * a.n_split + split;
+  for (int i = tid; i < G * D; i += kAttnThreads) {
+    const int g = i / D, d = i - g * D;
+    float mm = sh_m[0][g], ll = sh_l[0][g], oo = sh_o[0][g][d];
+#pragma unroll
+    for (int w = 1; w < kAttnWaves; ++w) merge<1>(mm, ll, &oo, sh_m[w][g], sh_l[w][g], &sh_o[w][g][d]);
+    const size_t pg = part + (size_t)g * a.n_split;
+    a.part_o[pg * D + d] = oo;
+    if (d == 0) {
+      a.part_ml[2 * pg] = mm;
+      a.part_ml[2 * pg + 1] = ll;
+    }
+  }
+}
+
 // out[b][g] = merge over splits; one workgroup per (sequence, query head).
 // Splits are read eight at a time (all loads of a batch issued before any is
 // used), then merged in split order.
@@ -312,8 +555,12 @@ __global__ __launch_bounds__(D) void combine_kernel(AttnArgs a) {
   constexpr int kB = 8;
   const int bg = blockIdx.x;
   const int d = threadIdx.x;
-  const int n = a.n_split;
-  const size_t p0 = (size_t)bg * n;
+  // the sequence's own splits (its clamped length, as in attention_kernel)
+  int L = a.lens[bg / a.Hq];
+  const int max_tok = a.MB * a.bs;
+  L = L < 1 ? 1 : (L > max_tok ? max_tok : L);
+  const int n = min(a.n_split, (L + a.chunk - 1) / a.chunk);
+  const size_t p0 = (size_t)bg * a.n_split;
   float mm = -INFINITY;
   for (int s0 = 0; s0 < n; s0 += kB) {
     float ms[kB];
@@ -346,7 +593,10 @@ __global__ __launch_bounds__(D) void combine_kernel(AttnArgs a) {
 template <typename T, int D, int G>
 hipError_t launch_attention_g(const AttnArgs& a, hipStream_t s) {
   const unsigned grid = (unsigned)a.S * a.Hkv * a.n_split;
-  hipLaunchKernelGGL((attention_kernel<T, D, G>), dim3(grid), dim3(kAttnThreads), 0, s, a);
+  if constexpr (sizeof(T) == 2)
+    hipLaunchKernelGGL((attention_mfma_kernel<D, G>), dim3(grid), dim3(kAttnThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((attention_kernel<T, D, G>), dim3(grid), dim3(kAttnThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((combine_kernel<D>), dim3((unsigned)a.S * a.Hq), dim3(D), 0, s, a);

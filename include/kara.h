@@ -355,7 +355,9 @@ size_t kara_attention_workspace_bytes(const kara_shape* shape, int32_t n_seqs, i
  *                clamped to the same range)
  *   workspace    dev, kara_attention_workspace_bytes(shape, n_seqs,
  *                max(seq_lens_h)) bytes, 256-byte aligned.
- * Supported: n_q_heads / n_kv_heads <= 8.  Block ids are clamped to the pool.
+ * Supported: n_q_heads / n_kv_heads <= 8, and n_blocks * n_kv_heads *
+ * block_size < 2^32 (a layer's K rows are numbered in 32 bits).  Block ids
+ * are clamped to the pool.
  * Errors: KARA_E_INVAL, KARA_E_UNSUPPORTED, KARA_E_WORKSPACE (nothing
  * written), KARA_E_HIP. */
 kara_status kara_decode_attention(const kara_shape* shape, int32_t n_seqs, int32_t layer,

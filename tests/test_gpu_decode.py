@@ -87,6 +87,44 @@ def test_decode_attention(name):
     say(name, "max error", worst)
 
 
+def test_decode_attention_large_launch_1024_token_splits():
+    """A launch with enough work for 1024-token splits (512 sequences of
+    1025-1100 tokens, 8 KV heads: at least 8192 workgroups of 1024 tokens),
+    Qwen3-14B-shaped heads (G = 5, D = 128); sampled sequences, including both
+    ends of the batch, against the oracle on their own blocks."""
+    say("decode attention, 1024-token splits")
+    S, Hq, Hkv, D, bs = 512, 40, 8, 128, 16
+    rng = np.random.default_rng(21)
+    lens = rng.integers(1025, 1101, S).astype(np.int32)
+    nblk = (lens + bs - 1) // bs
+    NB, MB = int(nblk.sum()), int(nblk.max())
+    assert int(((lens + 1023) // 1024).sum()) * Hkv >= 8192
+    perm = rng.permutation(NB).astype(np.int32)
+    table = np.full((S, MB), -1, dtype=np.int32)
+    off = np.concatenate([[0], np.cumsum(nblk)])
+    for b in range(S):
+        table[b, :nblk[b]] = perm[off[b]:off[b + 1]]
+    g = torch.Generator(device="cuda").manual_seed(22)
+    pool = torch.randn((1, 2, NB, Hkv, bs, D), generator=g, device="cuda").to(torch.bfloat16)
+    q = (torch.randn((S, Hq, D), generator=g, device="cuda") * 0.3).to(torch.bfloat16)
+    shape = kara.kara_shape(1, Hq, Hkv, D, bs, kara.KARA_BF16)
+    lens_h = torch.from_numpy(lens)
+    ws = torch.empty(kara.kara_attention_workspace_bytes(shape, S, int(lens.max())), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.full((S, Hq, D), float("nan"), device="cuda")
+    kara.kara_decode_attention(shape, 0, q, pool, torch.from_numpy(table).cuda(), lens_h, lens_h.cuda(), out, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    worst = 0.0
+    for b in [0, 1, 2, 100, 255, 256, 400, 509, 510, 511]:
+        blocks = torch.from_numpy(table[b, :nblk[b]].astype(np.int64)).cuda()
+        sub = pool.index_select(2, blocks).cpu().double().numpy()
+        want = ko.decode_attention(q[b].cpu().double().numpy(), sub, np.arange(nblk[b], dtype=np.int32),
+                                   int(lens[b]), 0, bs)
+        worst = max(worst, assert_attention_close(got[b], want, f"1024-token splits seq {b}"))
+    say("1024-token splits max error", worst)
+
+
 def test_decode_attention_validates():
     shape = kara.kara_shape(1, 18, 2, 128, 16, kara.KARA_BF16)     # G = 9
     lens = torch.tensor([5], dtype=torch.int32)

@@ -289,3 +289,15 @@ def test_plan_lengths_match_the_oracle_plan():
         kara.kara_plan_lengths(kara.kara_params(8, 2, 2, 3), 3, torch.tensor([10], dtype=torch.int32))
     with pytest.raises(kara.KaraError):
         kara.kara_plan_lengths(kara.kara_params(8, 2, 2, 3), 4, torch.tensor([7], dtype=torch.int32))
+
+
+def test_decode_attention_rejects_pools_beyond_32_bit_rows():
+    """Decode attention numbers a layer's K rows in 32 bits: a pool with
+    n_blocks * n_kv_heads * block_size >= 2^32 rows is refused before any
+    pointer is read."""
+    sh = shape(n_kv_heads=8, block_size=1024)
+    lens = (ctypes.c_int32 * 1)(5)
+    st = kara.lib.kara_decode_attention(ctypes.byref(sh), 1, 0, FAKE * 16, FAKE * 16, 1 << 19, FAKE * 16, 4,
+                                        lens, FAKE * 16, FAKE * 16, FAKE * 16, 1 << 30, None)
+    assert st == kara.KARA_E_UNSUPPORTED
+    assert "2^32" in kara.kara_last_error()
