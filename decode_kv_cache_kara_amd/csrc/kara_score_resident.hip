@@ -445,11 +445,8 @@ __device__ __forceinline__ void score_unit(const ScoreArgs& a, const int unit, R
 #pragma unroll
       for (int ks = 0; ks < kRKs - 1; ++ks) qa[ks] = qfrag(t + 1, ks);
       float rp[4];
-      // region k: the multiply of the lane's logit k, the exp2 of logit k - 1
-      // and the row-sum add of logit k - 2 (no operation waits on the one
-      // before it in its region), in place in `cur`
 #pragma unroll
-      for (int k = 0; k < 4 * NT + 2; ++k) {
+      for (int k = 0; k < 4 * NT; ++k) {
         if (k < 3 * NT) {
           const int ks = k / NT, nt = k % NT;
           if (ks == 0) {
@@ -459,14 +456,11 @@ __device__ __forceinline__ void score_unit(const ScoreArgs& a, const int unit, R
             nxt[nt] = mfma(qa[ks], kf[nt][ks], nxt[nt]);
           }
         }
-        if (k < 4 * NT) cur[k / 4][k % 4] *= c;
-        if (k >= 1 && k <= 4 * NT) {
-          const int j = k - 1;
-          cur[j / 4][j % 4] = __builtin_amdgcn_exp2f(cur[j / 4][j % 4]);
-        }
-        if (kRowSumsHere && k >= 2) {
-          const int j = k - 2, nt = j / 4, r = j % 4;
-          rp[r] = nt == 0 ? cur[nt][r] : rp[r] + cur[nt][r];
+        {
+          const int nt = k / 4, r = k % 4;
+          const float x = __builtin_amdgcn_exp2f(cur[nt][r] * c);
+          cur[nt][r] = x;
+          if (kRowSumsHere) rp[r] = nt == 0 ? x : rp[r] + x;
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -498,7 +492,7 @@ __device__ __forceinline__ void score_unit(const ScoreArgs& a, const int unit, R
       __builtin_amdgcn_sched_barrier(0);
       float w0 = wrow.x, w1 = wrow.y, w2 = wrow.z, w3 = wrow.w;
       if (kRowSumsHere) {
-        const float z = quad_sum(za + zb) + zx;
+        const float z = MODE == kWithRowSums ? quad_sum(za + zb) + zx : quad_sum(za + zb);
         const bool row_ok = t * kRRows + m < rows;
         if (MODE != kRowSums) bad |= __ballot(row_ok && !(z >= 0x1p-40f && z <= 0x1p100f)) != 0;
         if (MODE == kRowSums) {
