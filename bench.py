@@ -445,7 +445,9 @@ def run_trace(args, out_base):
                    "head_dim": cfg.head_dim, "window": W, "protect": cfg.protect, "top_k": cfg.top_k,
                    "budget": cfg.budget, "period": cfg.period, "lengths": f"{cfg.init_len}->{cfg.max_len}",
                    "events": tr.events, "compressions_timed": n_comp},
-        "roofline": {"bound": "mfma", "kernel": ("score_resident_kernel" if resident else "score_kernel"),
+        "roofline": {"bound": "mfma",
+                     "kernel": ("score_resident_kernel + exact_resident_kernel (marked units only)" if resident
+                                else "score_kernel"),
                      "achieved": round(score_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(score_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": None, "algorithmic_flop_total": score_flop,
@@ -537,7 +539,8 @@ def run_batch(cfg, args, flags, steps, warmup, extras=True, keep_outputs=False):
                    "not materialised (table entries before the boundary block are never read by the step)",
                    "ablation": {0: "none", 1: "unidirectional", 2: "no_chunks", 3: "unidirectional+no_chunks"}[flags]},
         "roofline": {"bound": "mfma",
-                     "kernel": ("score_resident_kernel" + (" (3 launches)" if W > 1024 else "")
+                     "kernel": (("score_resident_kernel (3 launches)" if W > 1024 else
+                                 "score_resident_kernel + exact_resident_kernel (marked units only)")
                                 if path == "resident" else "score_kernel"),
                      "achieved": round(score_tflops, 2),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(score_tflops / peak, 4),
