@@ -70,6 +70,15 @@ def test_static_scratch_matches_workspace_call_twice():
     _check_against_workspace_call(small, outputs=False)
 
 
+def test_static_scratch_two_key_block_windows():
+    """A 2048-key window (the scorer's three launches keep per-row normaliser
+    inputs and per-unit flags in the scratch too), after the one-block calls
+    above have left other contents in it."""
+    print("[case] static scratch: Qwen3-14B-shaped 2 seqs x 2 layers, W=2048", flush=True)
+    wl = synth.make_workload(3, device="cuda", n_seqs=2, n_layers=2)
+    _check_against_workspace_call(wl, outputs=True)
+
+
 def test_static_scratch_rejects_oversized_calls():
     print("[case] static scratch: oversized call rejected", flush=True)
     wl = synth.make_workload(2, device="cuda", n_seqs=2, n_layers=1)
