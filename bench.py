@@ -529,6 +529,7 @@ def run_batch(cfg, args, flags, steps, warmup, extras=True, keep_outputs=False):
 
     out = {
         "value": round(value, 1),
+        "token_layers_per_s": round(value * Lyr, 1),
         "ms_per_step": round(ms_per_step, 4),
         "dtype": "bf16" if wl.dtype == torch.bfloat16 else "f32",
         "config": {"workload": wl.name, "n_seqs": S, "n_layers": Lyr, "n_q_heads": Hq, "n_kv_heads": Hkv,
@@ -546,6 +547,7 @@ def run_batch(cfg, args, flags, steps, warmup, extras=True, keep_outputs=False):
                      "peak": peak, "unit": "TFLOP/s", "frac": round(score_tflops / peak, 4),
                      "traffic": traffic, "algorithmic_flop_per_launch": score_flop,
                      "executed_mfma_flop_per_launch": exec_flop if not uni else None,
+                     "executed_frac": (round(exec_flop / (stage[0] / 1e3) / 1e12 / peak, 4) if not uni else None),
                      "scorer": path, "kernel_source_sha256_16": kernel_source_hash()},
         "stages_ms": {"score": round(stage[0], 4), "select": round(stage[1], 4),
                       "compact": round(stage[2], 4)},
