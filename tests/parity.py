@@ -225,13 +225,23 @@ def _scores_job(args):
     return ko.window_scores(q, k, protect, unidirectional=uni)
 
 
-def oracle_scores_many(pairs, protect, unidirectional=False):
+def oracle_scores_many(pairs, protect, unidirectional=False, label=None):
     """The oracle's float64 window scores for a list of (q_window, k_window)
-    host arrays, computed in the CPU worker processes."""
+    host arrays, computed in the CPU worker processes.  With a label, a
+    progress line is printed about every 20 s while the results come in."""
+    import concurrent.futures as cf
+    import time
     jobs = [(q, k, protect, unidirectional) for q, k in pairs]
     if len(jobs) <= 2:
         return [_scores_job(j) for j in jobs]
-    return list(cpu_workers().map(_scores_job, jobs))
+    futs = [cpu_workers().submit(_scores_job, j) for j in jobs]
+    if label:
+        t0 = last = time.time()
+        for n, _ in enumerate(cf.as_completed(futs), 1):
+            if time.time() - last >= 20 or n == len(futs):
+                last = time.time()
+                print(f"[case] {label}: oracle scores {n}/{len(futs)} ({last - t0:.0f} s)", flush=True)
+    return [f.result() for f in futs]
 
 
 def pair_verdicts_job(args):

@@ -100,7 +100,8 @@ def test_full_size_sampled(cfg, flags):
     scores = gs_all.reshape(S, Lyr, Hkv, -1)
     cand = cand_all.reshape(S, Lyr, Hkv, -1)
     kept = kept_all.reshape(S, Lyr, Hkv, -1)
-    orc = oracle_scores_many([(snap[p]["q"], snap[p]["k"]) for p in samples], B, unidirectional=uni)
+    orc = oracle_scores_many([(snap[p]["q"], snap[p]["k"]) for p in samples], B, unidirectional=uni,
+                             label=f"config {cfg}")
     verdicts = {}
     worst = 0.0
     for (b, l), s in zip(samples, orc):
