@@ -50,17 +50,27 @@ def _replay_chunk(args):
 _POOL = None
 
 
+def _one_blas_thread():
+    """Worker initialiser: one BLAS thread per worker process, so that the
+    workers together use each core once."""
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(limits=1)
+
+
 def cpu_workers():
-    """CPU worker processes for large replays (spawned: they import NumPy and
-    the oracle only and never touch the GPU)."""
+    """CPU worker processes for large replays and oracle samples (spawned:
+    they import NumPy and the oracle only and never touch the GPU), one per
+    core this process may use, leaving one, with one BLAS thread each."""
     global _POOL
     if _POOL is None:
         import concurrent.futures
         import multiprocessing
         import os
-        n = max(1, min(8, len(os.sched_getaffinity(0)) - 1))
-        _POOL = concurrent.futures.ProcessPoolExecutor(max_workers=n,
+        n = max(1, min(15, len(os.sched_getaffinity(0)) - 1))
+        _POOL = concurrent.futures.ProcessPoolExecutor(max_workers=n, initializer=_one_blas_thread,
                                                        mp_context=multiprocessing.get_context("spawn"))
+        import atexit
+        atexit.register(_POOL.shutdown)
     return _POOL
 
 
