@@ -45,9 +45,9 @@
 // Registers (two waves per SIMD, at most 256 each): 4 NT x 4 for the keys,
 // 2 x 4 NT for two logit tiles (the next tile's MFMAs run while the VALU works
 // on the current one), 16 for the query fragments, NT column accumulators.
-// LDS: a ring of four 16-row query tiles (rows padded to 272 bytes), the
-// per-wave row sums, staged per-row normaliser inputs, and (exact route) one
-// reference and one normaliser per row.
+// LDS: a ring of six 16-row query tiles (4 KB each, moved from global memory
+// by direct-to-LDS loads), the per-wave row sums, staged per-row normaliser
+// inputs, and (exact route) one reference and one normaliser per row.
 
 #include "kara_internal.hpp"
 
@@ -63,8 +63,8 @@ constexpr int kRWaves = 8;
 constexpr int kRThreads = kRWaves * 64;
 constexpr int kRRows = 16;                     // query rows per tile
 constexpr int kRKs = 4;                        // 32-wide reduction steps over D = 128
-constexpr int kRQStride = 272;                 // LDS bytes per staged query row (256 + pad)
-constexpr int kRQSlots = 4;                    // query tiles in the LDS ring
+constexpr int kRQTile = kRRows * 256;          // LDS bytes of a staged query tile
+constexpr int kRQSlots = 6;                    // query tiles in the LDS ring
 constexpr int kRRowSlots = 8;                  // tiles of staged per-row inputs in LDS
 constexpr int kZStride = kRWaves + 1;          // floats per row of the per-wave row sums
 constexpr int kExactGrid = 512;                // workgroups of the exact launch (grid-stride)
@@ -125,13 +125,23 @@ __device__ __forceinline__ float row_bcast(float x) {
   return dpp<0x150 + 4 * kR>(x);
 }
 
+// 16 bytes per lane from global memory (base + off) straight into LDS: lane i
+// of the wave writes LDS bytes [lds + 16 i, lds + 16 i + 16).  The load counts
+// in vmcnt like any vector load; the caller waits for it before a barrier
+// that publishes the data (the compiler does not see the LDS write).
+__device__ __forceinline__ void load_to_lds16(const char* base, uint32_t off, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds) : "memory");
+}
+
+__device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 // LDS of one workgroup.
 struct ResidentLds {
-  __attribute__((aligned(16))) char qbuf[kRQSlots][kRRows * kRQStride];
+  __attribute__((aligned(16))) char qbuf[kRQSlots][kRQTile];
   __attribute__((aligned(16))) float zpart[2][kRWaves][kRRows];
   // fast pass: per-wave row sums as [row][wave] with a row stride of 9 floats,
   // so that neither the 16 writers of a wave nor the quads that read two
@@ -170,7 +180,7 @@ __device__ __forceinline__ void score_unit(const ScoreArgs& a, const int unit, R
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = lane >> 4;            // row group of the MFMA output: rows 4*grp .. 4*grp+3
   const int kl = lane & 15;             // key (output column) of the lane within an N-tile
 
@@ -224,33 +234,46 @@ __device__ __forceinline__ void score_unit(const ScoreArgs& a, const int unit, R
     return n_out;
   };
 
-  // ---- query tiles: global -> registers -> LDS ring ----
-  // Thread tid moves 8 bytes of a tile: row tid >> 5, bytes (tid & 31) * 8.
-  // Its row advances by 16 per tile, i.e. by 16 / G positions and 16 % G
-  // heads; the (position, head) pair is kept up to date incrementally.
-  const int st_row = tid >> 5;
-  const int st_off = (tid & 31) * 8;
-  const int di = kRRows / G, dg = kRRows - (kRRows / G) * G;
-  int ld_i = st_row / G, ld_g = st_row - (st_row / G) * G, ld_row = st_row;
-  // Loads the thread's piece of the next tile in sequence (tiles 0, 1, 2, ...).
-  // The load is unconditional, so that the compiler can wait for each piece by
-  // count rather than for every load in flight: rows past the last one read
-  // the last row again (finite values; their normaliser weights are zero).
-  // Offsets within the unit's window fit 32 bits (W * Hq * 256 bytes).
-  auto load_q = [&]() -> uint2 {
+  // ---- query tiles: global memory -> LDS ring ----
+  // A staged tile holds rows 16 t + kr, kr = 0..15, as four 1 KB quarters:
+  // quarter ks holds dims 32 ks .. 32 ks + 31 of every row, row kr at byte
+  // 64 kr of the quarter, its 16-byte piece p (dims 32 ks + 8 p ..) at
+  // position p ^ ((kr >> 2) & 3).  The 16 lanes that read one piece of rows
+  // 0..15 then meet in no LDS bank, and the quarter is an immediate offset.
+  //
+  // The fast pass moves two tiles per pair of steps with one direct-to-LDS load
+  // per wave: wave w moves quarter w & 3 of the pair's tile w >> 2, lane L row
+  // L >> 2, position L & 3.  The lane's row advances by 32 per pair, i.e. by
+  // 32 / G positions and 32 % G heads; the (position, head) pair is kept up to
+  // date incrementally.  Rows past the last one read the last row again
+  // (finite values; their normaliser weights are zero).  Offsets within the
+  // unit's window fit 32 bits (W * Hq * 256 bytes).
+  const uint32_t qlds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)&qbuf[0][0];
+  const int dm_row = 16 * (wave >> 2) + (lane >> 2);
+  const uint32_t dm_piece = (uint32_t)(4 * (wave & 3) + ((lane & 3) ^ ((lane >> 4) & 3))) * 16u;
+  const int di = 32 / G, dg = 32 - (32 / G) * G;
+  int ld_i = dm_row / G, ld_g = dm_row - (dm_row / G) * G, ld_row = dm_row;
+  // Starts the wave's load of the pair of tiles tp, tp + 1 (tp even, the next
+  // pair in sequence).
+  auto load_pair = [&](int tp) {
     const bool ok = ld_row < rows;
     const int i = ok ? ld_i : W - 1, g = ok ? ld_g : G - 1;
     const int slot_i = i + ring_off < W ? i + ring_off : i + ring_off - W;
-    const uint2 v = *(const uint2*)(qbase + ((uint32_t)(slot_i * a.Hq + g) * 256u + (uint32_t)st_off));
-    ld_row += kRRows;
+    const uint32_t off = (uint32_t)(slot_i * a.Hq + g) * 256u + dm_piece;
+    const int slot = (tp + (wave >> 2)) % kRQSlots;
+    load_to_lds16(qbase, off, qlds + (uint32_t)(slot * kRQTile + (wave & 3) * 1024));
+    ld_row += 32;
     ld_i += di;
     ld_g += dg;
     if (ld_g >= G) {
       ld_g -= G;
       ld_i += 1;
     }
-    return v;
   };
+  // Exact route: thread tid moves 8 bytes of a tile, row tid >> 5, bytes
+  // (tid & 31) * 8 of the row, through registers.
+  const int st_row = tid >> 5;
+  const int st_off = (tid & 31) * 8;
   // the thread's piece of tile t (random access, for the exact route)
   auto load_q_at = [&](int t) -> uint2 {
     const int row = t * kRRows + st_row;
@@ -259,14 +282,17 @@ __device__ __forceinline__ void score_unit(const ScoreArgs& a, const int unit, R
     const int slot_i = i + ring_off < W ? i + ring_off : i + ring_off - W;
     return *(const uint2*)(qbase + ((size_t)slot_i * a.Hq + g) * 256 + st_off);
   };
-  auto store_q = [&](uint2 v, int t) { *(uint2*)&qbuf[t % kRQSlots][st_row * kRQStride + st_off] = v; };
-  auto qfrag = [&](int t, int ks) -> bf16x8 {
-    return *(const bf16x8*)&qbuf[t % kRQSlots][kl * kRQStride + ks * 64 + grp * 16];
+  auto store_q = [&](uint2 v, int t) {
+    const int p = st_off >> 4;
+    const int pos = ((p & 3) ^ ((st_row >> 2) & 3)) * 16 + (st_off & 8);
+    *(uint2*)&qbuf[t % kRQSlots][(p >> 2) * 1024 + st_row * 64 + pos] = v;
   };
+  const int qlane = kl * 64 + ((grp ^ ((kl >> 2) & 3)) << 4);
+  auto qfrag = [&](int t, int ks) -> bf16x8 { return *(const bf16x8*)&qbuf[t % kRQSlots][ks * 1024 + qlane]; };
   // Per-row input of tile t (kWithRowSums: the partial normaliser over KB1;
-  // kWeighted: 1 / Z), staged through LDS like the query tiles and stored by
-  // threads 0..15 (0 for rows past the last one).  The load is unconditional
-  // for the same reason as the query pieces' (every wave reads row
+  // kWeighted: 1 / Z), staged through registers into LDS and stored by threads
+  // 0..15 (0 for rows past the last one).  The load is unconditional, so that
+  // the compiler can wait for it by count (every wave reads row
   // t * 16 + (tid & 15), clamped to the last row).
   auto load_row = [&](int t) -> float {
     if (!kStageRow) return 0.0f;
@@ -396,6 +422,9 @@ __device__ __forceinline__ void score_unit(const ScoreArgs& a, const int unit, R
 
   // ======================= fast pass: references 0 =========================
   const int key_lo = a.key_lo, key_hi = a.key_hi;
+  // the first two pairs of query tiles travel while the keys load
+  load_pair(0);
+  if (n_tiles > 2) load_pair(2);
   const float n_inval = load_keys(key_lo, key_hi);
   // keys past the block among the 16 lanes of the row group (logit 0, exp2 = 1)
   const float inval16 = row_sum16(n_inval);
@@ -404,34 +433,30 @@ __device__ __forceinline__ void score_unit(const ScoreArgs& a, const int unit, R
   for (int nt = 0; nt < NT; ++nt) colacc[nt] = 0.0f;
   bool bad = false;
   {
-    store_q(load_q(), 0);
-    store_q(load_q(), 1);
     store_row(load_row(0), 0);
     store_row(load_row(1), 1);
-    uint2 stg0 = load_q();
-    uint2 stg1 = load_q();
     float sr0 = load_row(2), sr1 = load_row(3);
+    wait_vm_all();
     __syncthreads();
     f32x4 acc0[NT], acc1[NT];
     tile_mfma(acc0, 0);
     // One tile: `cur` holds its logits, the next tile's go into `nxt`.  The
-    // first step of each pair (t even) stores tiles t + 2 and t + 3 (query
-    // pieces and row inputs loaded two steps earlier) to their LDS slots and
-    // fetches tiles t + 4 and t + 5, so that the loads in flight when a pair
-    // starts are a whole pair old.  The query slot of tile t + 3 last held
-    // tile t - 1, whose fragments were read before the previous step's
-    // barrier; the row inputs keep eight slots because a tile's are read after
-    // its barrier.
+    // first step of each pair (t even) waits for this wave's loads of tiles
+    // t + 2 and t + 3 (started two steps earlier; the step's barrier then
+    // publishes them), stores those tiles' row inputs, and starts the loads of
+    // tiles t + 4 and t + 5, so that the loads in flight when a pair starts
+    // are a whole pair old.  Tiles t + 4 and t + 5 go to the slots of tiles
+    // t - 2 and t - 1, whose fragments every wave read before the previous
+    // step's barrier; the row inputs keep eight slots because a tile's are
+    // read after its barrier.
     auto step = [&](f32x4 (&cur)[NT], f32x4 (&nxt)[NT], int t, bool stage) {
       if (stage) {
-        store_q(stg0, t + 2);
-        store_q(stg1, t + 3);
+        wait_vm_all();
         store_row(sr0, t + 2);
         store_row(sr1, t + 3);
-        stg0 = load_q();
-        stg1 = load_q();
         sr0 = load_row(t + 4);
         sr1 = load_row(t + 5);
+        if (t + 4 < n_tiles) load_pair(t + 4);
       }
       // The next tile's logits (past the last tile: zero rows, never used) on
       // the matrix cores while this tile's VALU work runs, in regions fenced
@@ -531,6 +556,9 @@ __device__ __forceinline__ void score_unit(const ScoreArgs& a, const int unit, R
       step(acc0, acc1, t, true);
       if (t + 1 < n_tiles) step(acc1, acc0, t + 1, false);
     }
+    // every tile load was waited for by a later pair; none may still be
+    // writing this workgroup's LDS when it ends
+    wait_vm_all();
   }
 
   if (MODE == kRowSums) return;
