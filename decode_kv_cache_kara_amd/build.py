@@ -24,6 +24,8 @@ FLAGS = [
     "-I", os.path.join(ROOT, "include"),
     "-Wno-unused-command-line-argument",
 ]
+# roctx ranges of the C ABI calls (rocprofv3 --marker-trace)
+LINK_LIBS = ["-L/opt/rocm/lib", "-lrocprofiler-sdk-roctx", "-Wl,-rpath,/opt/rocm/lib"]
 # the host pass does not know the packed-fp32 feature name; that warning is expected
 _NOISE = "is not a recognized feature for this target"
 
@@ -49,7 +51,7 @@ def build_library(verbose=False, extra_flags=(), out=None):
         with concurrent.futures.ThreadPoolExecutor(workers) as pool:
             errs = list(pool.map(_run, cmds))
         tmp = out + ".tmp"
-        errs.append(_run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp]))
+        errs.append(_run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + LINK_LIBS + ["-o", tmp]))
         if verbose:
             for c in cmds:
                 print(" ".join(c), flush=True)

@@ -6,6 +6,7 @@
 #include "kara_internal.hpp"
 
 #include <hip/hip_runtime.h>
+#include <rocprofiler-sdk-roctx/roctx.h>
 
 #include <cmath>
 #include <cstdarg>
@@ -25,6 +26,16 @@ struct kara_pool {
 namespace {
 
 thread_local std::string g_err;
+
+// A roctx range over a call that enqueues GPU work (shown by rocprofv3
+// --marker-trace next to the kernels it launched); without a tool attached a
+// push or pop is a call into an empty table.
+struct TraceRange {
+  explicit TraceRange(const char* name) { roctxRangePush(name); }
+  ~TraceRange() { roctxRangePop(); }
+  TraceRange(const TraceRange&) = delete;
+  TraceRange& operator=(const TraceRange&) = delete;
+};
 
 kara_status fail(kara_status s, const char* fmt, ...) {
   char buf[512];
@@ -413,7 +424,10 @@ kara_status compress_impl(const kara_shape* shape, const kara_params* params, in
     sa.q_counts = qs.ring->counts_d;
     sa.q_n_slots = qs.ring->n_slots;
   }
-  if ((e = kara::launch_score(sa, shape->dtype, s)) != hipSuccess) return hip_fail(e, "score launch");
+  {
+    TraceRange range("score");
+    if ((e = kara::launch_score(sa, shape->dtype, s)) != hipSuccess) return hip_fail(e, "score launch");
+  }
   if ((e = mark(1)) != hipSuccess) return hip_fail(e, "stage event");
   kara::SelectArgs se;
   se.partials = partials;
@@ -428,11 +442,17 @@ kara_status compress_impl(const kara_shape* shape, const kara_params* params, in
   se.R = params->budget;
   se.mode = kara::kSelectFull;
   se.no_chunks = (params->flags & KARA_NO_CHUNKS) ? 1 : 0;
-  if ((e = kara::launch_select(se, s)) != hipSuccess) return hip_fail(e, "select launch");
+  {
+    TraceRange range("select");
+    if ((e = kara::launch_select(se, s)) != hipSuccess) return hip_fail(e, "select launch");
+  }
   if ((e = mark(2)) != hipSuccess) return hip_fail(e, "stage event");
   kara::CompactArgs ca = compact_args(shape, params, n_seqs, kv_pool, n_blocks, block_table_d,
                                       new_block_table_d, max_blocks, seq_lens_d, retained);
-  if ((e = kara::launch_compact(ca, s)) != hipSuccess) return hip_fail(e, "compact launch");
+  {
+    TraceRange range("compact");
+    if ((e = kara::launch_compact(ca, s)) != hipSuccess) return hip_fail(e, "compact launch");
+  }
   if ((e = mark(3)) != hipSuccess) return hip_fail(e, "stage event");
   commit_plan(pool, plan);
   return KARA_OK;
@@ -450,6 +470,7 @@ kara_status kara_compress(const kara_shape* shape, const kara_params* params, in
                           int32_t* new_seq_lens_h, void* workspace, size_t workspace_bytes,
                           void* stream, float* scores_out_d, int32_t* cand_out_d,
                           int32_t* retained_out_d, void* const* stage_events) {
+  TraceRange range("kara_compress");
   return compress_impl(shape, params, n_seqs, QuerySource{q_window, nullptr}, kv_pool, n_blocks,
                        block_table_h, block_table_d, max_blocks, seq_lens_h, seq_lens_d, pool,
                        new_block_table_h, new_block_table_d, new_seq_lens_h, workspace,
@@ -466,6 +487,7 @@ kara_status kara_compress_ring(const kara_shape* shape, const kara_params* param
                                int32_t* new_seq_lens_h, void* workspace, size_t workspace_bytes,
                                void* stream, float* scores_out_d, int32_t* cand_out_d,
                                int32_t* retained_out_d, void* const* stage_events) {
+  TraceRange range("kara_compress_ring");
   if (!ring) return fail(KARA_E_INVAL, "query ring is NULL");
   return compress_impl(shape, params, n_seqs, QuerySource{ring->q_ring, ring}, kv_pool, n_blocks,
                        block_table_h, block_table_d, max_blocks, seq_lens_h, seq_lens_d, pool,
@@ -478,6 +500,7 @@ kara_status kara_append(const kara_shape* shape, int32_t window, int32_t n_seqs,
                         const void* q_d, const void* k_d, const void* v_d, void* kv_pool,
                         int32_t n_blocks, const int32_t* block_table_d, int32_t max_blocks,
                         const int32_t* positions_d, const kara_query_ring* ring, void* stream) {
+  TraceRange range("kara_append");
   kara_status st;
   if ((st = check_shape(shape)) != KARA_OK) return st;
   if (window < 1 || window > kara::kMaxWindow)
@@ -537,6 +560,7 @@ kara_status kara_decode_attention(const kara_shape* shape, int32_t n_seqs, int32
                                   const int32_t* seq_lens_h, const int32_t* seq_lens_d,
                                   float* out_d, void* workspace, size_t workspace_bytes,
                                   void* stream) {
+  TraceRange range("kara_decode_attention");
   kara_status st;
   if ((st = check_shape(shape)) != KARA_OK) return st;
   if (shape->n_q_heads / shape->n_kv_heads > 8)
@@ -599,6 +623,7 @@ kara_status kara_score(const kara_shape* shape, const kara_params* params, int32
                        const int32_t* block_table_h, const int32_t* block_table_d, int32_t max_blocks,
                        const int32_t* seq_lens_h, const int32_t* seq_lens_d, float* scores_d,
                        void* workspace, size_t workspace_bytes, void* stream) {
+  TraceRange range("kara_score");
   kara_status st;
   if ((st = check_shape(shape)) != KARA_OK) return st;
   if ((st = check_params(params)) != KARA_OK) return st;
@@ -630,6 +655,7 @@ kara_status kara_score(const kara_shape* shape, const kara_params* params, int32
 
 kara_status kara_topk(int32_t n_units, int32_t region, int32_t top_k, const float* scores_d,
                       int32_t* cand_d, void* stream) {
+  TraceRange range("kara_topk");
   if (n_units < 0) return fail(KARA_E_INVAL, "n_units < 0");
   if (region < 1 || region > kara::kMaxRegion) return fail(KARA_E_INVAL, "region %d outside [1, %d]", region, kara::kMaxRegion);
   if (top_k < 1 || top_k > region) return fail(KARA_E_INVAL, "top_k %d outside [1, %d]", top_k, region);
@@ -655,6 +681,7 @@ kara_status kara_topk(int32_t n_units, int32_t region, int32_t top_k, const floa
 kara_status kara_token2chunk(int32_t n_units, int32_t region, int32_t top_k, int32_t budget,
                              const float* scores_d, const int32_t* cand_d, int32_t* retained_d,
                              void* stream) {
+  TraceRange range("kara_token2chunk");
   if (n_units < 0) return fail(KARA_E_INVAL, "n_units < 0");
   if (region < 1 || region > kara::kMaxRegion) return fail(KARA_E_INVAL, "region %d outside [1, %d]", region, kara::kMaxRegion);
   if (top_k < 1 || top_k > region) return fail(KARA_E_INVAL, "top_k %d outside [1, %d]", top_k, region);
@@ -684,6 +711,7 @@ kara_status kara_paged_compact(const kara_shape* shape, const kara_params* param
                                const int32_t* seq_lens_h, const int32_t* seq_lens_d,
                                const int32_t* retained_d, kara_pool* pool, int32_t* new_block_table_h,
                                int32_t* new_block_table_d, int32_t* new_seq_lens_h, void* stream) {
+  TraceRange range("kara_paged_compact");
   kara_status st;
   if ((st = check_shape(shape)) != KARA_OK) return st;
   if ((st = check_params(params)) != KARA_OK) return st;
@@ -763,6 +791,7 @@ size_t kara_probe_scratch_bytes(void) {
 
 kara_status kara_probe(int32_t kind, int64_t iters, void* dst_d, const void* src_d, size_t n_bytes, void* stream,
                        double* work_out) {
+  TraceRange range("kara_probe");
   if (!work_out) return fail(KARA_E_INVAL, "work_out is NULL");
   if (kind < KARA_PROBE_MFMA || kind > KARA_PROBE_MIX) return fail(KARA_E_INVAL, "probe kind %d unknown", kind);
   const int n_cu = device_cus();
@@ -831,6 +860,7 @@ kara_status kara_compress_static(const kara_shape* shape, const kara_params* par
                                  kara_pool* pool, int32_t* new_block_table_h, int32_t* new_block_table_d,
                                  int32_t* new_seq_lens_h, void* stream, float* scores_out_d,
                                  int32_t* cand_out_d, int32_t* retained_out_d, void* const* stage_events) {
+  TraceRange range("kara_compress_static");
   kara_status st;
   if ((st = check_shape(shape)) != KARA_OK) return st;
   if ((st = check_params(params)) != KARA_OK) return st;

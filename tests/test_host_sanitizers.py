@@ -40,7 +40,7 @@ def test_host_code_under_address_and_ub_sanitizers():
         with concurrent.futures.ThreadPoolExecutor(max(1, min(8, os.cpu_count() or 1))) as pool:
             list(pool.map(build._run, cmds))
         exe = os.path.join(tmp, "host_driver")
-        build._run([build.HIPCC, "--offload-arch=gfx950"] + SAN + objs + [drv, "-o", exe])
+        build._run([build.HIPCC, "--offload-arch=gfx950"] + SAN + objs + [drv] + build.LINK_LIBS + ["-o", exe])
         env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=0:halt_on_error=1",
                    UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
         r = subprocess.run([exe], capture_output=True, text=True, timeout=300, env=env)
