@@ -77,6 +77,21 @@ SCORE_CASES = {
     "resident-w1100-g3": dict(n_seqs=2, n_layers=1, n_q_heads=6, n_kv_heads=2, head_dim=128, block_size=16,
                               window=1100, protect=50, top_k=60, budget=300, lens=(1100, 3000),
                               dtype=torch.bfloat16, qk_std=0.4),
+    # query rows move 32 per pair of tiles, i.e. 32 / G positions and 32 % G
+    # heads: one head per position (G = 1), a carry on most pairs (G = 7, one
+    # and two key blocks), and more heads than 32 (G = 40: no position step)
+    "resident-w333-g1": dict(n_seqs=2, n_layers=1, n_q_heads=3, n_kv_heads=3, head_dim=128, block_size=16,
+                             window=333, protect=33, top_k=20, budget=90, lens=(333, 1200),
+                             dtype=torch.bfloat16, qk_std=0.4),
+    "resident-w700-g7": dict(n_seqs=2, n_layers=1, n_q_heads=14, n_kv_heads=2, head_dim=128, block_size=16,
+                             window=700, protect=60, top_k=30, budget=150, lens=(700, 2100),
+                             dtype=torch.bfloat16, qk_std=0.3),
+    "resident-w1300-g7": dict(n_seqs=1, n_layers=2, n_q_heads=7, n_kv_heads=1, head_dim=128, block_size=16,
+                              window=1300, protect=100, top_k=50, budget=260, lens=[2900],
+                              dtype=torch.bfloat16, qk_std=0.3),
+    "resident-w40-g40": dict(n_seqs=2, n_layers=1, n_q_heads=40, n_kv_heads=1, head_dim=128, block_size=8,
+                             window=40, protect=4, top_k=6, budget=14, lens=(40, 99),
+                             dtype=torch.bfloat16, qk_std=0.4),
 }
 
 
