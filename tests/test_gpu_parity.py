@@ -92,6 +92,10 @@ SCORE_CASES = {
     "resident-w40-g40": dict(n_seqs=2, n_layers=1, n_q_heads=40, n_kv_heads=1, head_dim=128, block_size=8,
                              window=40, protect=4, top_k=6, budget=14, lens=(40, 99),
                              dtype=torch.bfloat16, qk_std=0.4),
+    # the largest unit the resident scorer takes: G * W = 16384 rows
+    "resident-w2048-g8-max-rows": dict(n_seqs=1, n_layers=1, n_q_heads=8, n_kv_heads=1, head_dim=128,
+                                       block_size=16, window=2048, protect=200, top_k=64, budget=500,
+                                       lens=[2600], dtype=torch.bfloat16, qk_std=0.3),
 }
 
 
@@ -114,16 +118,16 @@ def test_score_stage(name):
     say(name, "max rel err", worst)
 
 
-@pytest.mark.parametrize("window", [256, 1600])
-def test_score_stage_exact_fallback(window):
+@pytest.mark.parametrize("window,n_q_heads", [(256, 8), (1600, 8), (2048, 16)])
+def test_score_stage_exact_fallback(window, n_q_heads):
     """One key made ~110 nats more attractive to one query than that query's
     first keys: with the first keys' maximum as the row's reference the sum
     would overflow float, so the workgroup must redo its row statistics with a
     running maximum.  The scores still match the oracle."""
-    say("score stage exact fallback")
-    wl = gpu_workload(None, n_seqs=2, n_layers=1, n_q_heads=8, n_kv_heads=2, head_dim=128, block_size=16,
-                      window=window, protect=32, top_k=8, budget=40, lens=[window + 44, window + 444],
-                      dtype=torch.bfloat16, qk_std=0.1)
+    say("score stage exact fallback, window", window, "query heads", n_q_heads)
+    wl = gpu_workload(None, n_seqs=2, n_layers=1, n_q_heads=n_q_heads, n_kv_heads=2, head_dim=128,
+                      block_size=16, window=window, protect=32, top_k=8, budget=40,
+                      lens=[window + 44, window + 444], dtype=torch.bfloat16, qk_std=0.1)
     b, i, j = 0, 150, 200                      # sequence, query position, key position (window-local)
     q = wl.q_window[b, 0, i, 0].float()        # query head 0 belongs to KV head 0
     s = 110.0 * math.sqrt(128) / float(q @ q)
