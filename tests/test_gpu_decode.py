@@ -178,12 +178,14 @@ def test_append_writes_cache_rows_and_ring(layer):
     assert torch.equal(bits(rd.cpu()), bits(want_ring))
 
 
-@pytest.mark.parametrize("cfg", [0, 1])
+@pytest.mark.parametrize("cfg", [0, 1, 3])
 def test_compress_ring_equals_compress(cfg):
     """The same windows, once as an array and once scattered into a ring with
-    arbitrary slots and token counts, give bit-identical results."""
+    arbitrary slots and token counts, give bit-identical results (cfg 3's
+    shape: the two-key-block scorer)."""
     say("compress ring", cfg)
-    over = dict(n_seqs=3, n_layers=2, lens=(1100, 3000)) if cfg == 1 else {}
+    over = {1: dict(n_seqs=3, n_layers=2, lens=(1100, 3000)),
+            3: dict(n_seqs=2, n_layers=2, lens=(2100, 4000))}.get(cfg, {})
     wl = synth.make_workload(cfg, device="cuda", **over)
     S, Lyr, W = wl.n_seqs, wl.n_layers, wl.window
     n_slots = S + 3
