@@ -51,12 +51,15 @@ def gen_length(cfg, i):
 
 def simulate(cfg):
     """Returns (summary dict, per-step list of (running after the step,
-    compressions in the step, step time))."""
+    compressions in the step, step time)).  The summary's `admissions` lists
+    request ids in admission order, re-admissions after a preemption
+    included."""
     bs = cfg["block_size"]
     free = cfg["cap_blocks"]
     running = []           # dicts: req, len, left, gen, wm, blocks
     waiting = list(range(cfg["n_requests"]))
     steps = []
+    admissions = []
     tokens = stalls = compressions = peak = preemptions = wasted = 0
     total_ms = compress_ms = 0.0
     step = 0
@@ -68,6 +71,7 @@ def simulate(cfg):
                 break
             free -= need
             req = waiting.pop(0)
+            admissions.append(req)
             running.append(dict(req=req, len=cfg["prompt_len"], left=gen_length(cfg, req), gen=0, wm=0,
                                 blocks=need))
         ms = cfg["decode_ms_fixed"] + cfg["decode_ms_per_token"] * sum(s["len"] for s in running)
@@ -128,5 +132,5 @@ def simulate(cfg):
                    preemptions=preemptions, wasted=wasted,
                    finished=cfg["n_requests"] - len(running) - len(waiting), total_ms=total_ms,
                    compress_ms=compress_ms,
-                   mean_active=(sum(a for a, _, _ in steps) / step) if step else 0.0)
+                   mean_active=(sum(a for a, _, _ in steps) / step) if step else 0.0, admissions=admissions)
     return summary, steps

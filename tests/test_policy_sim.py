@@ -85,6 +85,54 @@ def test_memory_cap_stalls_and_preemption():
     assert s2["finished"] == 12 and s2["wasted"] < s["wasted"]
 
 
+def test_rule_request_lengths_cover_the_range():
+    """gen_min + x % (gen_max - gen_min + 1): over 200 requests every length
+    from gen_min to gen_max occurs, and none outside."""
+    cfg = base(gen_min=7, gen_max=10, seed=123)
+    assert {po.gen_length(cfg, i) for i in range(200)} == {7, 8, 9, 10}
+
+
+def test_rule_blocks_follow_the_length():
+    """One request, no compression: a block is taken whenever a token is
+    appended at a length that is a multiple of the block size, so after a step
+    the sequence holds ceil(length / bs) blocks.  The peak is read at the end
+    of a step, after finished sequences left, so it is the count at the end of
+    the second-to-last step, length prompt + gen - 1 (none for gen = 1).
+    Lengths on both sides of block boundaries."""
+    for prompt, gen in [(16, 2), (16, 17), (16, 18), (17, 16), (17, 17), (5, 12), (5, 13), (16, 1)]:
+        cfg = base(prompt_len=prompt, gen_min=gen, gen_max=gen, window=10_000)
+        s, _ = po.simulate(cfg)
+        want = -(-(prompt + gen - 1) // 16) if gen > 1 else 0
+        assert s["peak_blocks"] == want, (prompt, gen)
+
+
+def test_rule_periodic_new_length():
+    """Prompt of W tokens, period 1, gen 50 < W - B: one compression, at step
+    1, from W + 1 tokens to (W + 1) - (W - B) + R; step k >= 2 then starts
+    with B + R + k - 1 tokens.  The total time is the sum of the step costs."""
+    W, B, R, g = 128, 16, 24, 50
+    cfg = base(prompt_len=W, gen_min=g, gen_max=g, window=W, protect=B, budget=R)
+    s, _ = po.simulate(cfg)
+    cached = W + sum(B + R + k - 1 for k in range(2, g + 1))
+    assert s["compressions"] == 1
+    assert abs(s["total_ms"] - (g * 2.0 + 1e-3 * cached + 0.5)) < 1e-9
+
+
+def test_rule_preempted_request_returns_to_the_front():
+    """Block size 1, prompt 1, 4 blocks, 2 slots, 3 requests of 3 tokens
+    (traced by hand from the rules): step 1 admits 0 and 1 (2 blocks left,
+    both append); step 2 both stall, 1 (the newest) is preempted and goes back
+    to the front; step 3 re-admits 1, only 0 appends; step 4 both stall and 1
+    is preempted again; step 5 admits nobody (one free block, one spare
+    needed), 0 finishes; step 6 admits 1, then 2."""
+    cfg = base(policy="none", n_requests=3, max_batch=2, cap_blocks=4, block_size=1, prompt_len=1,
+               gen_min=3, gen_max=3, window=10_000)
+    s, steps = po.simulate(cfg)
+    assert s["admissions"][:5] == [0, 1, 1, 1, 2]
+    assert s["preemptions"] >= 2 and s["finished"] == 3
+    assert [a for a, _, _ in steps[:5]] == [2, 1, 2, 1, 0]
+
+
 @pytest.mark.parametrize("seed", range(8))
 @pytest.mark.parametrize("policy", ["periodic", "threshold", "none"])
 def test_native_simulator_equals_oracle(policy, seed):
