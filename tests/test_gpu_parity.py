@@ -338,6 +338,70 @@ def test_compress_end_to_end(name):
         assert verdicts.get("exact", 0) == wl.n_units   # well-separated scores: no ties to adjudicate
 
 
+def random_resident_case(seed):
+    """A seeded shape for the resident-key scorer (bf16, head size 128): W over
+    1..2048 (one or two key blocks), G = 1..8 with G * W <= 16384 rows, one or
+    two KV heads, a random protected tail, K and R anywhere in [1, C] with
+    R >= K, ragged sequence lengths, and a random logit scale."""
+    rng = np.random.default_rng(7000 + seed)
+    W = int(rng.choice([int(rng.integers(1, 200)), int(rng.integers(200, 1025)), int(rng.integers(1025, 2049))]))
+    G = int(rng.integers(1, 9))
+    while G * W > 16384:
+        G -= 1
+    Hkv = int(rng.integers(1, 3))
+    B = int(rng.integers(0, max(1, W // 4)))
+    C = W - B
+    K = int(rng.integers(1, C + 1))
+    R = int(rng.integers(K, C + 1)) if C > K else C
+    return dict(n_seqs=2, n_layers=1, n_q_heads=G * Hkv, n_kv_heads=Hkv, head_dim=128, block_size=16,
+                window=W, protect=B, top_k=K, budget=R, lens=(W, W + int(rng.integers(0, 3000))),
+                dtype=torch.bfloat16, qk_std=float(rng.choice([0.1, 0.3, 0.6])))
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_compress_end_to_end_random_resident_shapes(seed):
+    p = random_resident_case(seed)
+    say("compress end to end, random resident shape", seed, {k: p[k] for k in ("window", "protect", "top_k",
+                                                                              "budget", "n_q_heads", "n_kv_heads")})
+    wl = gpu_workload(None, seed=7000 + seed, **p)
+    orc = oracle_scores(wl)
+    ses, pool, before = run_e2e(wl)
+    verdicts = check_e2e(wl, ses, pool, before, orc, case="e2e random resident shapes")
+    say(seed, verdicts)
+
+
+def random_twopass_case(seed):
+    """A seeded shape for the two-pass scorer: float32 (head size 64 or 128),
+    bf16 with head size 64, or bf16 / 128 with a window over 2048 keys."""
+    rng = np.random.default_rng(8000 + seed)
+    kind = int(rng.integers(0, 4))
+    dtype = torch.float32 if kind <= 1 else torch.bfloat16
+    D = 64 if kind in (0, 2) else 128
+    W = int(rng.integers(2049, 4097)) if kind == 3 else int(rng.integers(1, 1200))
+    G = int(rng.integers(1, 5 if kind == 3 else 9))
+    Hkv = int(rng.integers(1, 3))
+    B = int(rng.integers(0, max(1, W // 4)))
+    C = min(W - B, 2048)
+    B = W - C
+    K = int(rng.integers(1, C + 1))
+    R = int(rng.integers(K, C + 1)) if C > K else C
+    return dict(n_seqs=2, n_layers=1, n_q_heads=G * Hkv, n_kv_heads=Hkv, head_dim=D,
+                block_size=int(rng.choice([8, 16])), window=W, protect=B, top_k=K, budget=R,
+                lens=(W, W + int(rng.integers(0, 3000))), dtype=dtype, qk_std=float(rng.choice([0.1, 0.3, 0.6])))
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_compress_end_to_end_random_twopass_shapes(seed):
+    p = random_twopass_case(seed)
+    say("compress end to end, random two-pass shape", seed, {k: str(p[k]) for k in (
+        "window", "protect", "top_k", "budget", "n_q_heads", "n_kv_heads", "head_dim", "dtype")})
+    wl = gpu_workload(None, seed=8000 + seed, **p)
+    orc = oracle_scores(wl)
+    ses, pool, before = run_e2e(wl)
+    verdicts = check_e2e(wl, ses, pool, before, orc, case="e2e random two-pass shapes")
+    say(seed, verdicts)
+
+
 def test_compress_matches_oracle_end_to_end_exactly_when_sets_agree():
     """Where the oracle's selection is reproduced, the whole step (cache bytes,
     tables, lengths, free list) equals the oracle's compress() output."""
