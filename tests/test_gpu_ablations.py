@@ -148,6 +148,37 @@ def test_ablation_end_to_end(name, flags):
     say(name, flags, verdicts)
 
 
+def random_ablation_case(seed):
+    """A seeded shape and ablation: flags 1, 2 or 3; bf16 or float32, head size
+    64 or 128, W = 1 … 1500, G = 1 … 8, random B, K and R (R below K too)."""
+    rng = np.random.default_rng(9000 + seed)
+    flags = int(rng.integers(1, 4))
+    dtype = torch.bfloat16 if rng.random() < 0.7 else torch.float32
+    D = 128 if rng.random() < 0.7 else 64
+    W = int(rng.choice([int(rng.integers(1, 100)), int(rng.integers(100, 1501))]))
+    G = int(rng.integers(1, 9))
+    Hkv = int(rng.integers(1, 3))
+    B = int(rng.integers(0, max(1, W // 4)))
+    C = W - B
+    K = int(rng.integers(1, C + 1))
+    R = int(rng.integers(1, C + 1))
+    return flags, dict(n_seqs=2, n_layers=1, n_q_heads=G * Hkv, n_kv_heads=Hkv, head_dim=D,
+                       block_size=int(rng.choice([8, 16])), window=W, protect=B, top_k=K, budget=R,
+                       lens=(W, W + int(rng.integers(0, 2000))), dtype=dtype,
+                       qk_std=float(rng.choice([0.1, 0.3, 0.6])))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_ablation_end_to_end_random_shapes(seed):
+    flags, p = random_ablation_case(seed)
+    say("ablation end to end, random shape", seed, "flags", flags,
+        {k: str(p[k]) for k in ("window", "protect", "top_k", "budget", "n_q_heads", "n_kv_heads", "head_dim",
+                                "dtype")})
+    wl = synth.make_workload(None, seed=9000 + seed, device="cpu", **p).to("cuda")
+    verdicts = check_flags_e2e(wl, flags, case=f"ablation random shapes flags {flags}")
+    say(seed, flags, verdicts)
+
+
 def test_no_chunks_differs_from_token2chunk():
     """On planted spans the Token2Chunk result and the top-R set differ."""
     say("no-chunks differs")
