@@ -62,12 +62,9 @@ ATT_CASES = {
 }
 
 
-@pytest.mark.parametrize("name", list(ATT_CASES))
-def test_decode_attention(name):
-    say("decode attention", name)
-    c = ATT_CASES[name]
-    pool, table = random_cache(11, c["S"], c["Lyr"], c["Hkv"], c["D"], c["bs"], c["lens"], c["dtype"])
-    g = torch.Generator().manual_seed(12)
+def run_attention_case(name, c, cache_seed=11, q_seed=12):
+    pool, table = random_cache(cache_seed, c["S"], c["Lyr"], c["Hkv"], c["D"], c["bs"], c["lens"], c["dtype"])
+    g = torch.Generator().manual_seed(q_seed)
     q = (torch.randn((c["S"], c["Hq"], c["D"]), generator=g) * c["qs"]).to(c["dtype"])
     shape = kara.kara_shape(c["Lyr"], c["Hq"], c["Hkv"], c["D"], c["bs"], kara.dtype_code(c["dtype"]))
     lens_h = torch.tensor(c["lens"], dtype=torch.int32)
@@ -84,7 +81,39 @@ def test_decode_attention(name):
         for b in range(c["S"]):
             want = ko.decode_attention(q[b].double().numpy(), pn, table[b].numpy(), c["lens"][b], layer, c["bs"])
             worst = max(worst, assert_attention_close(got[b], want, f"{name} seq {b} layer {layer}"))
+    return worst
+
+
+@pytest.mark.parametrize("name", list(ATT_CASES))
+def test_decode_attention(name):
+    say("decode attention", name)
+    worst = run_attention_case(name, ATT_CASES[name])
     say(name, "max error", worst)
+
+
+def random_attention_case(seed):
+    """A seeded decode-attention shape: 1-6 sequences, 1-2 layers, G = 1 … 8,
+    1-4 KV heads, head size 64 or 128, block size 4, 8 or 16, bf16 or float32,
+    lengths from 1 to 5000 with some placed at the 512- and 1024-token split
+    boundaries."""
+    rng = np.random.default_rng(9500 + seed)
+    S = int(rng.integers(1, 7))
+    Hkv = int(rng.integers(1, 5))
+    G = int(rng.integers(1, 9))
+    edges = [1, 511, 512, 513, 1023, 1024, 1025, 2048, 2049]
+    lens = [int(rng.choice(edges)) if rng.random() < 0.4 else int(rng.integers(1, 5001)) for _ in range(S)]
+    return dict(S=S, Lyr=int(rng.integers(1, 3)), Hq=G * Hkv, Hkv=Hkv, D=int(rng.choice([64, 128])),
+                bs=int(rng.choice([4, 8, 16])), lens=lens,
+                dtype=torch.bfloat16 if rng.random() < 0.7 else torch.float32,
+                qs=float(rng.choice([0.1, 0.5, 1.5])))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_decode_attention_random_shapes(seed):
+    c = random_attention_case(seed)
+    say("decode attention, random shape", seed, {k: str(v) for k, v in c.items()})
+    worst = run_attention_case(f"random {seed}", c, cache_seed=100 + seed, q_seed=200 + seed)
+    say(seed, "max error", worst)
 
 
 def test_decode_attention_large_launch_1024_token_splits():
