@@ -39,6 +39,9 @@
  *   cand      [n_seqs][n_layers][n_kv_heads][K] int32, ascending
  *   retained  [n_seqs][n_layers][n_kv_heads][R] int32, ascending, in [0, C)
  * Window-local position i of sequence b is token lens[b] - W + i.
+ * q_window, kv_pool and a query ring must be 16-byte aligned (the kernels move
+ * 16-byte pieces, the scorer straight from global memory into LDS); other
+ * base addresses return KARA_E_INVAL.
  *
  * Ownership: the caller owns every buffer and the stream.  The library never
  * allocates device memory; kara_compress and kara_score use a caller-provided
