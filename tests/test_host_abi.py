@@ -119,9 +119,9 @@ class Call:
         self.ws = over.pop("ws", kara.kara_workspace_bytes(self.shape, self.params, len(self.lens)))
         assert not over
 
-    def run(self):
+    def run(self, q=FAKE * 16, kv=FAKE * 16):
         return kara.lib.kara_compress(
-            ctypes.byref(self.shape), ctypes.byref(self.params), len(self.lens), FAKE * 16, FAKE * 16,
+            ctypes.byref(self.shape), ctypes.byref(self.params), len(self.lens), q, kv,
             self.n_blocks, self.table, FAKE * 16, self.max_blocks, _i32(self.lens), FAKE * 16,
             self.pool.handle, self.new_table, FAKE * 16, self.new_lens, 256 * 16, self.ws, None,
             None, None, None, None)
@@ -147,6 +147,18 @@ def test_compress_rejects_before_side_effects(kw, status):
     before = c.pool.snapshot()
     assert c.run() == status, kara.kara_last_error()
     assert kara.kara_last_error()
+    assert c.pool.snapshot() == before
+    assert list(c.new_lens) == [0, 0]
+
+
+@pytest.mark.parametrize("arg", ["q", "kv"])
+def test_compress_rejects_misaligned_state_arrays(arg):
+    """The query states and the pool must be 16-byte aligned; an 8-byte offset
+    is rejected before any side effect."""
+    c = Call()
+    before = c.pool.snapshot()
+    assert c.run(**{arg: FAKE * 16 + 8}) == kara.KARA_E_INVAL
+    assert "aligned" in kara.kara_last_error()
     assert c.pool.snapshot() == before
     assert list(c.new_lens) == [0, 0]
 
