@@ -260,6 +260,38 @@ def measured_ceilings(score_ms, exec_flop, exec_logits, compact_ms, compact_byte
     }
 
 
+def _probe_note(da):
+    if "paged_read_probe_gbs" not in da:
+        return ""
+    return f"; its loads alone {da['paged_read_probe_gbs']:.0f} GB/s ({da['frac_of_paged_read']:.1%} of them)"
+
+
+def paged_read_ceiling(shape, layers, pool, table_d, lens_h, lens_d, attention_gbs, stream, launches=20):
+    """The same launches' loads alone (kara_probe_paged_read: the attention
+    kernel's workgroups, block-id staging and 16-byte K and V row loads, no
+    arithmetic), cycling through `layers`; returns the probe's rate and the
+    attention kernel's rate as a fraction of it."""
+    import torch
+
+    from decode_kv_cache_kara_amd import kara
+
+    dst = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for k in range(3):
+        kara.kara_probe_paged_read(shape, k % layers, pool, table_d, lens_h, lens_d, dst, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    nbytes = 0.0
+    for k in range(launches):
+        nbytes = kara.kara_probe_paged_read(shape, k % layers, pool, table_d, lens_h, lens_d, dst, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / launches
+    gbs = nbytes / (ms / 1e3) / 1e9
+    return {"paged_read_probe_gbs": round(gbs, 1), "paged_read_probe_ms": round(ms, 4),
+            "frac_of_paged_read": round(attention_gbs / gbs, 4)}
+
+
 def decode_attention_roofline(ses, wl, launches=36):
     """Decode attention over the cache as the last compression step left it
     (new tables and lengths): HBM bytes per launch = K and V rows of every
@@ -292,10 +324,13 @@ def decode_attention_roofline(ses, wl, launches=36):
     tokens = int(lens_h.sum())
     nbytes = 2.0 * tokens * wl.n_kv_heads * D * wl.pool.element_size()
     gbs = nbytes / (ms / 1e3) / 1e9
-    return {"bound": "hbm", "kernel": "attention_kernel+combine_kernel", "achieved": round(gbs, 1),
-            "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-            "ms_per_launch": round(ms, 4), "algorithmic_bytes_per_launch": nbytes,
-            "cached_tokens": tokens, "note": "one layer of all sequences over the compacted cache"}
+    res = {"bound": "hbm", "kernel": "attention_kernel+combine_kernel", "achieved": round(gbs, 1),
+           "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+           "ms_per_launch": round(ms, 4), "algorithmic_bytes_per_launch": nbytes,
+           "cached_tokens": tokens, "note": "one layer of all sequences over the compacted cache"}
+    if wl.dtype == torch.bfloat16:
+        res.update(paged_read_ceiling(ses.shape, Lyr, wl.pool, table_d, lens_h, lens_d, gbs, stream))
+    return res
 
 
 def decode_attention_one_layer(wl, lens_h, launches=20):
@@ -345,14 +380,17 @@ def decode_attention_one_layer(wl, lens_h, launches=20):
     tokens = int(lens.sum())
     nbytes = 2.0 * tokens * Hkv * D * pool.element_size()
     gbs = nbytes / (ms / 1e3) / 1e9
+    res = {"bound": "hbm", "kernel": "attention_kernel+combine_kernel", "achieved": round(gbs, 1),
+           "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+           "ms_per_launch": round(ms, 4), "algorithmic_bytes_per_launch": nbytes,
+           "cached_tokens": tokens,
+           "note": ("one layer of the workload's shape at the lengths the compression step left, every block "
+                    f"materialised with random values ({NB} blocks, {nbytes / 2**30:.1f} GiB), fragmented tables")}
+    if wl.dtype == torch.bfloat16:
+        res.update(paged_read_ceiling(shape, 1, pool, table_d, lens_h32, lens_d, gbs, stream))
     del pool
     torch.cuda.empty_cache()
-    return {"bound": "hbm", "kernel": "attention_kernel+combine_kernel", "achieved": round(gbs, 1),
-            "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-            "ms_per_launch": round(ms, 4), "algorithmic_bytes_per_launch": nbytes,
-            "cached_tokens": tokens,
-            "note": ("one layer of the workload's shape at the lengths the compression step left, every block "
-                     f"materialised with random values ({NB} blocks, {nbytes / 2**30:.1f} GiB), fragmented tables")}
+    return res
 
 
 def policy_sim(out, wl):
@@ -560,11 +598,12 @@ def run_batch(cfg, args, flags, steps, warmup, extras=True, keep_outputs=False):
     if extras and materialized:
         out["decode_attention"] = decode_attention_roofline(ses, wl)
         log(f"decode attention over the compacted cache: {out['decode_attention']['ms_per_launch']:.3f} ms/layer, "
-            f"{out['decode_attention']['achieved']:.0f} GB/s")
+            f"{out['decode_attention']['achieved']:.0f} GB/s{_probe_note(out['decode_attention'])}")
     elif extras:
         out["decode_attention"] = decode_attention_one_layer(wl, ses.new_lens_h)
         log(f"decode attention over a one-layer cache at the compacted lengths: "
-            f"{out['decode_attention']['ms_per_launch']:.3f} ms/layer, {out['decode_attention']['achieved']:.0f} GB/s")
+            f"{out['decode_attention']['ms_per_launch']:.3f} ms/layer, {out['decode_attention']['achieved']:.0f} GB/s"
+            f"{_probe_note(out['decode_attention'])}")
     if extras and wl.dtype == torch.bfloat16 and not uni:
         exec_logits = exec_flop / (2.0 * D)
         out["measured_ceilings"] = measured_ceilings(stage[0], exec_flop, exec_logits, stage[2], compact_bytes)

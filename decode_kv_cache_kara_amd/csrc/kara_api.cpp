@@ -281,6 +281,61 @@ kara::CompactArgs compact_args(const kara_shape* sh, const kara_params* p, int32
 
 bool is_aligned(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
 
+// Validation and launch arguments shared by decode attention and its
+// paged-read probe (everything but the query states, outputs and workspace).
+kara_status attention_args(const kara_shape* shape, int32_t n_seqs, int32_t layer, const void* kv_pool,
+                           int32_t n_blocks, const int32_t* block_table_d, int32_t max_blocks,
+                           const int32_t* seq_lens_h, const int32_t* seq_lens_d, kara::AttnArgs* a,
+                           int32_t* max_len_out) {
+  kara_status st;
+  if ((st = check_shape(shape)) != KARA_OK) return st;
+  if (shape->n_q_heads / shape->n_kv_heads > 8)
+    return fail(KARA_E_UNSUPPORTED, "decode attention supports at most 8 query heads per KV head");
+  if (n_seqs < 0) return fail(KARA_E_INVAL, "n_seqs < 0");
+  if (layer < 0 || layer >= shape->n_layers)
+    return fail(KARA_E_INVAL, "layer %d outside [0, %d)", layer, shape->n_layers);
+  if (n_blocks < 1 || max_blocks < 1) return fail(KARA_E_INVAL, "n_blocks and max_blocks must be >= 1");
+  // the kernels index a layer's K rows with 32-bit row numbers
+  if ((uint64_t)n_blocks * shape->n_kv_heads * shape->block_size >= ((uint64_t)1 << 32))
+    return fail(KARA_E_UNSUPPORTED, "n_blocks * n_kv_heads * block_size = %llu rows per layer exceed 2^32",
+                (unsigned long long)n_blocks * shape->n_kv_heads * shape->block_size);
+  *max_len_out = 0;
+  if (n_seqs == 0) return KARA_OK;
+  if (!seq_lens_h) return fail(KARA_E_INVAL, "host lengths NULL");
+  int32_t max_len = 0;
+  for (int32_t b = 0; b < n_seqs; ++b) {
+    const int64_t L = seq_lens_h[b];
+    if (L < 1 || L > (int64_t)max_blocks * shape->block_size)
+      return fail(KARA_E_INVAL, "sequence %d: length %lld outside [1, max_blocks * block_size]", b, (long long)L);
+    max_len = L > max_len ? (int32_t)L : max_len;
+  }
+  if (!kv_pool || !block_table_d || !seq_lens_d) return fail(KARA_E_INVAL, "device pointer NULL");
+  if (!is_aligned(kv_pool, 16)) return fail(KARA_E_INVAL, "q and kv_pool must be 16-byte aligned");
+  a->q = nullptr;
+  a->pool = kv_pool;
+  a->table = block_table_d;
+  a->lens = seq_lens_d;
+  a->part_o = a->part_ml = a->out = nullptr;
+  a->S = n_seqs;
+  a->layer = layer;
+  a->Hq = shape->n_q_heads;
+  a->Hkv = shape->n_kv_heads;
+  a->D = shape->head_dim;
+  a->bs = shape->block_size;
+  a->bs_shift = log2_exact(shape->block_size);
+  a->NB = n_blocks;
+  a->MB = max_blocks;
+  // 1024-token splits when they alone give the launch enough workgroups
+  long big_grid = 0;
+  for (int32_t b = 0; b < n_seqs; ++b) big_grid += ceil_div(seq_lens_h[b], kara::kAttnChunkMax);
+  big_grid *= shape->n_kv_heads;
+  a->chunk = big_grid >= kara::kAttnBigGrid ? kara::kAttnChunkMax : kara::kAttnChunkMin;
+  a->n_split = ceil_div(max_len, a->chunk);
+  a->c = (float)(1.4426950408889634 / std::sqrt((double)shape->head_dim));
+  *max_len_out = max_len;
+  return KARA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -561,61 +616,45 @@ kara_status kara_decode_attention(const kara_shape* shape, int32_t n_seqs, int32
                                   float* out_d, void* workspace, size_t workspace_bytes,
                                   void* stream) {
   TraceRange range("kara_decode_attention");
-  kara_status st;
-  if ((st = check_shape(shape)) != KARA_OK) return st;
-  if (shape->n_q_heads / shape->n_kv_heads > 8)
-    return fail(KARA_E_UNSUPPORTED, "decode attention supports at most 8 query heads per KV head");
-  if (n_seqs < 0) return fail(KARA_E_INVAL, "n_seqs < 0");
-  if (layer < 0 || layer >= shape->n_layers)
-    return fail(KARA_E_INVAL, "layer %d outside [0, %d)", layer, shape->n_layers);
-  if (n_blocks < 1 || max_blocks < 1) return fail(KARA_E_INVAL, "n_blocks and max_blocks must be >= 1");
-  // the kernel indexes a layer's K rows with 32-bit row numbers
-  if ((uint64_t)n_blocks * shape->n_kv_heads * shape->block_size >= ((uint64_t)1 << 32))
-    return fail(KARA_E_UNSUPPORTED, "n_blocks * n_kv_heads * block_size = %llu rows per layer exceed 2^32",
-                (unsigned long long)n_blocks * shape->n_kv_heads * shape->block_size);
-  if (n_seqs == 0) return KARA_OK;
-  if (!seq_lens_h) return fail(KARA_E_INVAL, "host lengths NULL");
+  kara::AttnArgs a;
   int32_t max_len = 0;
-  for (int32_t b = 0; b < n_seqs; ++b) {
-    const int64_t L = seq_lens_h[b];
-    if (L < 1 || L > (int64_t)max_blocks * shape->block_size)
-      return fail(KARA_E_INVAL, "sequence %d: length %lld outside [1, max_blocks * block_size]", b, (long long)L);
-    max_len = L > max_len ? (int32_t)L : max_len;
-  }
-  if (!q_d || !kv_pool || !block_table_d || !seq_lens_d || !out_d)
-    return fail(KARA_E_INVAL, "device pointer NULL");
-  if (!is_aligned(q_d, 16) || !is_aligned(kv_pool, 16))
-    return fail(KARA_E_INVAL, "q and kv_pool must be 16-byte aligned");
+  kara_status st = attention_args(shape, n_seqs, layer, kv_pool, n_blocks, block_table_d, max_blocks, seq_lens_h,
+                                  seq_lens_d, &a, &max_len);
+  if (st != KARA_OK || n_seqs == 0) return st;
+  if (!q_d || !out_d) return fail(KARA_E_INVAL, "device pointer NULL");
+  if (!is_aligned(q_d, 16)) return fail(KARA_E_INVAL, "q and kv_pool must be 16-byte aligned");
   const size_t need = kara_attention_workspace_bytes(shape, n_seqs, max_len);
   if (!workspace || workspace_bytes < need || !is_aligned(workspace, kAlign))
     return fail(KARA_E_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned", need);
-  kara::AttnArgs a;
   a.q = q_d;
-  a.pool = kv_pool;
-  a.table = block_table_d;
-  a.lens = seq_lens_d;
-  a.S = n_seqs;
-  a.layer = layer;
-  a.Hq = shape->n_q_heads;
-  a.Hkv = shape->n_kv_heads;
-  a.D = shape->head_dim;
-  a.bs = shape->block_size;
-  a.bs_shift = log2_exact(shape->block_size);
-  a.NB = n_blocks;
-  a.MB = max_blocks;
-  // 1024-token splits when they alone give the launch enough workgroups
-  long big_grid = 0;
-  for (int32_t b = 0; b < n_seqs; ++b) big_grid += ceil_div(seq_lens_h[b], kara::kAttnChunkMax);
-  big_grid *= shape->n_kv_heads;
-  a.chunk = big_grid >= kara::kAttnBigGrid ? kara::kAttnChunkMax : kara::kAttnChunkMin;
-  a.n_split = ceil_div(max_len, a.chunk);
-  a.c = (float)(1.4426950408889634 / std::sqrt((double)shape->head_dim));
   const size_t parts = (size_t)n_seqs * a.Hq * a.n_split;
   a.part_o = (float*)workspace;
   a.part_ml = (float*)((char*)workspace + align_up(parts * a.D * sizeof(float)));
   a.out = out_d;
   const hipError_t e = kara::launch_attention(a, shape->dtype, (hipStream_t)stream);
   return e == hipSuccess ? KARA_OK : hip_fail(e, "attention launch");
+}
+
+kara_status kara_probe_paged_read(const kara_shape* shape, int32_t n_seqs, int32_t layer, const void* kv_pool,
+                                  int32_t n_blocks, const int32_t* block_table_d, int32_t max_blocks,
+                                  const int32_t* seq_lens_h, const int32_t* seq_lens_d, void* dst_d,
+                                  void* stream, double* bytes_out) {
+  TraceRange range("kara_probe_paged_read");
+  if (!bytes_out) return fail(KARA_E_INVAL, "bytes_out is NULL");
+  if (shape && shape->dtype != KARA_BF16)
+    return fail(KARA_E_UNSUPPORTED, "the paged-read probe mirrors the bf16 attention kernel only");
+  kara::AttnArgs a;
+  int32_t max_len = 0;
+  kara_status st = attention_args(shape, n_seqs, layer, kv_pool, n_blocks, block_table_d, max_blocks, seq_lens_h,
+                                  seq_lens_d, &a, &max_len);
+  if (st != KARA_OK) return st;
+  double bytes = 0.0;
+  for (int32_t b = 0; b < n_seqs; ++b) bytes += (double)seq_lens_h[b];
+  *bytes_out = bytes * a.Hkv * 2.0 * a.D * 2.0;
+  if (n_seqs == 0) return KARA_OK;
+  if (!dst_d || !is_aligned(dst_d, 4)) return fail(KARA_E_INVAL, "dst NULL or not 4-byte aligned");
+  const hipError_t e = kara::launch_paged_read_probe(a, (uint32_t*)dst_d, (hipStream_t)stream);
+  return e == hipSuccess ? KARA_OK : hip_fail(e, "probe launch");
 }
 
 kara_status kara_score(const kara_shape* shape, const kara_params* params, int32_t n_seqs,

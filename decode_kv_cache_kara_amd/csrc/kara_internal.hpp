@@ -128,6 +128,8 @@ struct AttnArgs {
 };
 
 hipError_t launch_attention(const AttnArgs& a, int dtype, hipStream_t stream);
+// The bf16 attention kernel's loads alone (a measurement aid; dst: 4 bytes).
+hipError_t launch_paged_read_probe(const AttnArgs& a, uint32_t* dst, hipStream_t stream);
 
 struct CompactArgs {
   void* pool;                 // [Lyr][2][NB][Hkv][bs][D]

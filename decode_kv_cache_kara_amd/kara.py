@@ -115,6 +115,7 @@ _SIGS = {
                                   _P]),
     "kara_probe_scratch_bytes": (ctypes.c_size_t, []),
     "kara_probe": (_I, [_I, ctypes.c_int64, _P, _P, ctypes.c_size_t, _P, ctypes.POINTER(ctypes.c_double)]),
+    "kara_probe_paged_read": (_I, [_P, _I, _I, _P, _I, _P, _I, _P, _P, _P, _P, ctypes.POINTER(ctypes.c_double)]),
 }
 EXPORTED = tuple(_SIGS)
 
@@ -399,6 +400,18 @@ def kara_decode_attention(shape, layer, q, kv_pool, block_table_d, seq_lens_h, s
         _host_i32(seq_lens_h, "seq_lens_h"), _dev(seq_lens_d, "seq_lens_d", torch.int32),
         _dev(out, "out", torch.float32), _dev(workspace, "workspace"),
         workspace.numel() * workspace.element_size() if workspace is not None else 0, _stream(stream)))
+
+
+def kara_probe_paged_read(shape, layer, kv_pool, block_table_d, seq_lens_h, seq_lens_d, dst, stream=None):
+    """Enqueues the paged-read probe (see include/kara.h); returns the bytes it reads."""
+    n_seqs = seq_lens_h.numel()
+    nbytes = ctypes.c_double(0.0)
+    _check(_lib.kara_probe_paged_read(
+        ctypes.byref(shape), n_seqs, int(layer), _dev(kv_pool, "kv_pool"), kv_pool.shape[2],
+        _dev(block_table_d, "block_table_d", torch.int32), block_table_d.shape[1],
+        _host_i32(seq_lens_h, "seq_lens_h"), _dev(seq_lens_d, "seq_lens_d", torch.int32), _dev(dst, "dst"),
+        _stream(stream), ctypes.byref(nbytes)))
+    return nbytes.value
 
 
 def _sim_config(cfg):

@@ -497,6 +497,25 @@ size_t kara_probe_scratch_bytes(void);
 kara_status kara_probe(int32_t kind, int64_t iters, void* dst_d, const void* src_d, size_t n_bytes, void* stream,
                        double* work_out);
 
+/* Measurement aid, not part of the compression step: the memory traffic of
+ * kara_decode_attention (bf16) alone, to set that kernel's rate against what
+ * the same access pattern reaches on this device.  Takes the arguments of
+ * kara_decode_attention except the query states, output and workspace, with
+ * the same meaning, layout, validation and errors (KARA_E_UNSUPPORTED also for
+ * a float32 shape), and launches a kernel with the same workgroup
+ * decomposition (one split of 512 or 1024 tokens of one sequence and KV head
+ * per workgroup, chosen by the same rule), the same block-id staging and the
+ * same 16-byte loads of every cached token's K and V rows of `layer`, with no
+ * arithmetic.  dst_d: 4 bytes of device memory, 4-byte aligned (written only
+ * if the loaded words fold to a fixed value, in practice never).
+ * *bytes_out receives the bytes the launch reads by definition:
+ * sum(seq_lens_h) * n_kv_heads * 2 * head_dim * 2.  Enqueued on `stream`;
+ * the caller times it. */
+kara_status kara_probe_paged_read(const kara_shape* shape, int32_t n_seqs, int32_t layer, const void* kv_pool,
+                                  int32_t n_blocks, const int32_t* block_table_d, int32_t max_blocks,
+                                  const int32_t* seq_lens_h, const int32_t* seq_lens_d, void* dst_d,
+                                  void* stream, double* bytes_out);
+
 #ifdef __cplusplus
 }
 #endif

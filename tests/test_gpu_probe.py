@@ -56,3 +56,35 @@ def test_probe_rejects_bad_arguments(kara):
     odd = torch.zeros(17, dtype=torch.uint8, device="cuda")
     with pytest.raises(kara.KaraError):
         kara.kara_probe(kara.KARA_PROBE_COPY, 1, odd, src=odd.clone())
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_paged_read_probe(kara, D):
+    """The paged-read probe (decode attention's loads alone) runs over a
+    fragmented cache with lengths around the split sizes, reports the K and V
+    bytes of every cached token of the layer, leaves its 4-byte destination
+    alone, and rejects a float32 shape before launching."""
+    S, Lyr, Hq, Hkv, bs = 5, 2, 20, 4, 16
+    lens = [1, 511, 512, 1025, 3000]
+    nblk = [-(-L // bs) for L in lens]
+    NB, MB = sum(nblk) + 3, max(nblk)
+    g = torch.Generator().manual_seed(3)
+    perm = torch.randperm(NB, generator=g).to(torch.int32)
+    table = torch.full((S, MB), -1, dtype=torch.int32)
+    cur = 0
+    for b in range(S):
+        table[b, :nblk[b]] = perm[cur:cur + nblk[b]]
+        cur += nblk[b]
+    pool = torch.randn((Lyr, 2, NB, Hkv, bs, D), device="cuda").to(torch.bfloat16)
+    lens_h = torch.tensor(lens, dtype=torch.int32)
+    dst = torch.zeros(1, dtype=torch.int32, device="cuda")
+    shape = kara.kara_shape(Lyr, Hq, Hkv, D, bs, kara.dtype_code(torch.bfloat16))
+    for layer in range(Lyr):
+        nbytes = kara.kara_probe_paged_read(shape, layer, pool, table.cuda(), lens_h, lens_h.cuda(), dst)
+        torch.cuda.synchronize()
+        assert nbytes == sum(lens) * Hkv * 2 * D * 2
+    assert int(dst.item()) == 0
+    shape32 = kara.kara_shape(Lyr, Hq, Hkv, D, bs, kara.dtype_code(torch.float32))
+    with pytest.raises(kara.KaraError) as e:
+        kara.kara_probe_paged_read(shape32, 0, pool.float(), table.cuda(), lens_h, lens_h.cuda(), dst)
+    assert e.value.status == kara.KARA_E_UNSUPPORTED
