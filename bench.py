@@ -222,9 +222,11 @@ def measured_ceilings(score_ms, exec_flop, exec_logits, compact_ms, compact_byte
     src = torch.ones(n // 4, dtype=torch.int32, device="cuda")
     dst = torch.empty_like(src)
 
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+
     def rate(kind, iters, launches):
-        kw = {"src": src} if kind == kara.KARA_PROBE_COPY else {}
-        out_t = dst if kind == kara.KARA_PROBE_COPY else scratch
+        kw = {"src": src} if kind in (kara.KARA_PROBE_COPY, kara.KARA_PROBE_READ) else {}
+        out_t = {kara.KARA_PROBE_COPY: dst, kara.KARA_PROBE_READ: sink, kara.KARA_PROBE_WRITE: dst}.get(kind, scratch)
         kara.kara_probe(kind, iters, out_t, stream=stream, **kw)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
@@ -236,14 +238,18 @@ def measured_ceilings(score_ms, exec_flop, exec_logits, compact_ms, compact_byte
     mfma = rate(kara.KARA_PROBE_MFMA, 100000, 3)          # flop/s
     valu = rate(kara.KARA_PROBE_VALU, 50000, 3)           # elements/s
     mix = rate(kara.KARA_PROBE_MIX, 10000, 3)             # logits/s
-    copy = rate(kara.KARA_PROBE_COPY, 1, 3)               # bytes/s
-    del src, dst, scratch
+    copy = rate(kara.KARA_PROBE_COPY, 1, 3)               # bytes/s (read + written)
+    read = rate(kara.KARA_PROBE_READ, 1, 3)               # bytes/s
+    write = rate(kara.KARA_PROBE_WRITE, 1, 3)             # bytes/s
+    del src, dst, scratch, sink
     bound_ms = exec_logits / mix * 1e3
     return {
         "mfma_bf16_tflops": round(mfma / 1e12, 1),
         "valu_softmax_gelem_per_s": round(valu / 1e9, 1),
         "mix_glogits_per_s": round(mix / 1e9, 1),
         "copy_gbs": round(copy / 1e9, 1),
+        "read_gbs": round(read / 1e9, 1),
+        "write_gbs": round(write / 1e9, 1),
         "score_kernel": {
             "executed_logits_per_launch": exec_logits,
             "mfma_alone_ms": round(exec_flop / mfma * 1e3, 3),
@@ -609,7 +615,8 @@ def run_batch(cfg, args, flags, steps, warmup, extras=True, keep_outputs=False):
         out["measured_ceilings"] = measured_ceilings(stage[0], exec_flop, exec_logits, stage[2], compact_bytes)
         mc = out["measured_ceilings"]
         log(f"measured ceilings: MFMA {mc['mfma_bf16_tflops']} TFLOP/s, softmax VALU {mc['valu_softmax_gelem_per_s']} "
-            f"Gelem/s, interleaved {mc['mix_glogits_per_s']} Glogit/s, copy {mc['copy_gbs']} GB/s; score kernel at "
+            f"Gelem/s, interleaved {mc['mix_glogits_per_s']} Glogit/s, copy {mc['copy_gbs']} GB/s (read "
+            f"{mc['read_gbs']}, write {mc['write_gbs']}); score kernel at "
             f"{mc['score_kernel']['frac_of_interleaved']:.1%} of its interleaved bound")
     gpu = None
     if keep_outputs:

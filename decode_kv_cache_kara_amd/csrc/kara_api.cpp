@@ -832,7 +832,7 @@ kara_status kara_probe(int32_t kind, int64_t iters, void* dst_d, const void* src
                        double* work_out) {
   TraceRange range("kara_probe");
   if (!work_out) return fail(KARA_E_INVAL, "work_out is NULL");
-  if (kind < KARA_PROBE_MFMA || kind > KARA_PROBE_MIX) return fail(KARA_E_INVAL, "probe kind %d unknown", kind);
+  if (kind < KARA_PROBE_MFMA || kind > KARA_PROBE_WRITE) return fail(KARA_E_INVAL, "probe kind %d unknown", kind);
   const int n_cu = device_cus();
   if (n_cu < 1) return fail(KARA_E_HIP, "no current HIP device");
   if (!dst_d) return fail(KARA_E_INVAL, "dst is NULL");
@@ -840,6 +840,13 @@ kara_status kara_probe(int32_t kind, int64_t iters, void* dst_d, const void* src
     if (!src_d) return fail(KARA_E_INVAL, "src is NULL");
     if (n_bytes % 16 != 0 || !is_aligned(dst_d, 16) || !is_aligned(src_d, 16))
       return fail(KARA_E_INVAL, "copy probe: size and both addresses must be multiples of 16");
+  } else if (kind == KARA_PROBE_READ) {
+    if (!src_d) return fail(KARA_E_INVAL, "src is NULL");
+    if (n_bytes % 16 != 0 || !is_aligned(src_d, 16) || !is_aligned(dst_d, 4))
+      return fail(KARA_E_INVAL, "read probe: size and src must be multiples of 16, dst of 4");
+  } else if (kind == KARA_PROBE_WRITE) {
+    if (n_bytes % 16 != 0 || !is_aligned(dst_d, 16))
+      return fail(KARA_E_INVAL, "write probe: size and dst must be multiples of 16");
   } else {
     if (iters < 1) return fail(KARA_E_INVAL, "iters must be >= 1");
     if (n_bytes < (size_t)kara::probe_grid(n_cu) * 256 * sizeof(float))

@@ -12,7 +12,11 @@
 //           interleaves them: while the VALU turns one 64x32 logit tile into
 //           exponentials and sums, the matrix cores compute the next tile
 //           (2 * 128 MFMA flops per logit), in eight fenced regions of two
-//           MFMAs and four logits each.
+//           MFMAs and four logits each;
+//   kind 4  a streaming read with the copy's loads and launch shape; the loaded
+//           words are XOR-folded and stored only if they fold to a fixed
+//           value (in practice never), so nothing is written;
+//   kind 5  a streaming write with the copy's stores and launch shape.
 // Kinds 0, 1 and 3 run two waves per SIMD, the scoring kernel's occupancy.
 // This is a measurement aid of the benchmark, not part of the compression step.
 
@@ -122,6 +126,34 @@ __global__ __launch_bounds__(kProbeThreads) void probe_copy(u32x4* __restrict__ 
   }
 }
 
+__global__ __launch_bounds__(kProbeThreads) void probe_read(uint32_t* sink, const u32x4* __restrict__ src,
+                                                           int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * kProbeThreads;
+  u32x4 fold = {0u, 0u, 0u, 0u};
+  for (int64_t i0 = (int64_t)blockIdx.x * kProbeThreads + threadIdx.x; i0 < n; i0 += stride * kCopyUnroll) {
+    u32x4 v[kCopyUnroll];
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      v[u] = i0 + u * stride < n ? __builtin_nontemporal_load(src + i0 + u * stride) : z;
+    }
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) fold ^= v[u];
+  }
+  const uint32_t w = fold.x ^ fold.y ^ fold.z ^ fold.w;
+  if (w == 0x9E3779B9u) sink[0] = w;
+}
+
+__global__ __launch_bounds__(kProbeThreads) void probe_write(u32x4* __restrict__ dst, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * kProbeThreads;
+  const u32x4 val = {threadIdx.x, blockIdx.x, 0x5A5A5A5Au, 1u};
+  for (int64_t i0 = (int64_t)blockIdx.x * kProbeThreads + threadIdx.x; i0 < n; i0 += stride * kCopyUnroll) {
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u)
+      if (i0 + u * stride < n) __builtin_nontemporal_store(val, dst + i0 + u * stride);
+  }
+}
+
 }  // namespace
 
 int probe_grid(int n_cu) { return 2 * n_cu; }
@@ -145,6 +177,20 @@ hipError_t launch_probe(int kind, int64_t iters, void* dst, const void* src, siz
       const unsigned g = (unsigned)(16 * n_cu);
       hipLaunchKernelGGL(probe_copy, dim3(g), dim3(kProbeThreads), 0, stream, (u32x4*)dst, (const u32x4*)src, n);
       *work = 2.0 * (double)n * 16.0;                                 // bytes read + written
+      break;
+    }
+    case 4: {
+      const int64_t n = (int64_t)(n_bytes / 16);
+      const unsigned g = (unsigned)(16 * n_cu);
+      hipLaunchKernelGGL(probe_read, dim3(g), dim3(kProbeThreads), 0, stream, (uint32_t*)dst, (const u32x4*)src, n);
+      *work = (double)n * 16.0;                                       // bytes read
+      break;
+    }
+    case 5: {
+      const int64_t n = (int64_t)(n_bytes / 16);
+      const unsigned g = (unsigned)(16 * n_cu);
+      hipLaunchKernelGGL(probe_write, dim3(g), dim3(kProbeThreads), 0, stream, (u32x4*)dst, n);
+      *work = (double)n * 16.0;                                       // bytes written
       break;
     }
     case 3:

@@ -451,6 +451,8 @@ KARA_PROBE_MFMA = 0
 KARA_PROBE_VALU = 1
 KARA_PROBE_COPY = 2
 KARA_PROBE_MIX = 3
+KARA_PROBE_READ = 4
+KARA_PROBE_WRITE = 5
 
 
 def kara_probe_scratch_bytes():
@@ -461,8 +463,9 @@ def kara_probe(kind, iters, dst, src=None, stream=None):
     """Enqueues one measurement probe (see include/kara.h); returns its work
     (flops, elements, bytes read + written, or logits by kind)."""
     work = ctypes.c_double(0.0)
-    if src is not None and src.numel() * src.element_size() < dst.numel() * dst.element_size():
+    if kind == KARA_PROBE_COPY and src is not None and src.numel() * src.element_size() < dst.numel() * dst.element_size():
         raise ValueError("src is smaller than dst")
+    n_bytes = (src if kind == KARA_PROBE_READ and src is not None else dst)
     _check(_lib.kara_probe(int(kind), int(iters), _dev(dst, "dst"), None if src is None else _dev(src, "src"),
-                           dst.numel() * dst.element_size(), _stream(stream), ctypes.byref(work)))
+                           n_bytes.numel() * n_bytes.element_size(), _stream(stream), ctypes.byref(work)))
     return work.value

@@ -482,17 +482,26 @@ kara_status kara_policy_sim(const kara_sim_config* config, kara_sim_result* resu
  *                    and order of the scoring kernel's inner loop (2 * 128
  *                    bf16 MFMA flops and one multiply-add, exp2 and add per
  *                    logit); work in logits.
+ *   KARA_PROBE_READ  a streaming read of n_bytes from src_d with the copy's
+ *                    loads and launch shape; dst_d is a 4-byte sink (written
+ *                    only if the loaded words fold to a fixed value, in
+ *                    practice never); work in bytes read.
+ *   KARA_PROBE_WRITE a streaming write of n_bytes to dst_d with the copy's
+ *                    stores and launch shape (src_d unused); work in bytes
+ *                    written.
  * MFMA, VALU and MIX run `iters` loop iterations in each of two waves per
  * SIMD and write one float per thread to dst_d, which must hold
- * kara_probe_scratch_bytes() bytes (n_bytes gives its size).  COPY ignores
- * iters; n_bytes and both addresses must be multiples of 16.  The launch is
+ * kara_probe_scratch_bytes() bytes (n_bytes gives its size).  COPY, READ and
+ * WRITE ignore iters; n_bytes and their buffer addresses must be multiples
+ * of 16 (READ's sink: of 4).  The launch is
  * enqueued on `stream` (the caller times it, e.g. with events); *work_out
  * receives the launch's work in the unit above.  dst_d and src_d are
  * caller-owned device buffers; src_d must hold n_bytes.  KARA_E_INVAL on bad
  * arguments (nothing launched); KARA_E_HIP when there is no current device or
  * the launch fails.  kara_probe_scratch_bytes() returns 0 when there is no
  * current device. */
-enum { KARA_PROBE_MFMA = 0, KARA_PROBE_VALU = 1, KARA_PROBE_COPY = 2, KARA_PROBE_MIX = 3 };
+enum { KARA_PROBE_MFMA = 0, KARA_PROBE_VALU = 1, KARA_PROBE_COPY = 2, KARA_PROBE_MIX = 3, KARA_PROBE_READ = 4,
+       KARA_PROBE_WRITE = 5 };
 size_t kara_probe_scratch_bytes(void);
 kara_status kara_probe(int32_t kind, int64_t iters, void* dst_d, const void* src_d, size_t n_bytes, void* stream,
                        double* work_out);

@@ -88,3 +88,17 @@ def test_paged_read_probe(kara, D):
     with pytest.raises(kara.KaraError) as e:
         kara.kara_probe_paged_read(shape32, 0, pool.float(), table.cuda(), lens_h, lens_h.cuda(), dst)
     assert e.value.status == kara.KARA_E_UNSUPPORTED
+
+
+def test_read_and_write_probes(kara):
+    """The read probe reads its buffer and leaves the sink alone; the write
+    probe fills its buffer; both report their bytes."""
+    n = (1 << 20) + 48
+    src = torch.randint(0, 255, (n,), dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    assert kara.kara_probe(kara.KARA_PROBE_READ, 1, sink, src=src) == float(n)
+    dst = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    assert kara.kara_probe(kara.KARA_PROBE_WRITE, 1, dst) == float(n)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 0
+    assert int((dst.view(torch.int32)[2::4] == 0x5A5A5A5A).sum()) == n // 16   # every 16-byte piece written
