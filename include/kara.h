@@ -53,8 +53,11 @@
  * effect.  A non-OK status from validation means nothing changed (pool, host
  * outputs and device memory are untouched).  KARA_E_HIP means a HIP call
  * failed after validation; work already enqueued may have run and the stream
- * should be treated as poisoned.  kara_last_error() returns a message for the
- * last non-OK status of the calling thread.
+ * should be treated as poisoned.  A kara_pool is changed only by a call that
+ * returns KARA_OK (on KARA_E_HIP the fresh blocks stay free and the old ones
+ * stay with their sequences), but the host outputs of kara_compress may
+ * already hold the planned tables and lengths.  kara_last_error() returns a
+ * message for the last non-OK status of the calling thread.
  *
  * Ordering: kernels are enqueued on `stream` (a hipStream_t; NULL is the null
  * stream) and the calls return without waiting for them.  Host outputs are
