@@ -1,5 +1,5 @@
 """Property test of the C ABI's front end (no GPU): for random kara_compress
-arguments, valid or not, a non-OK status leaves the block pool unchanged, and
+(and kara_paged_compact) arguments, valid or not, a non-OK status leaves the block pool unchanged, and
 every status but KARA_E_HIP also leaves the host outputs untouched, with a
 message from kara_last_error().  On a machine without a GPU every call ends
 non-OK (an argument error, or KARA_E_HIP at the first device call), so the
@@ -122,6 +122,33 @@ def test_failed_calls_change_nothing(c):
         FAKE if ws else None, ws, None, None, None, None, None)
     if st_ == kara.KARA_OK:
         assert n == 0                            # only an empty batch succeeds without a device
+        return
+    assert kara.kara_last_error()
+    assert pool.snapshot() == before
+    if st_ != kara.KARA_E_HIP:
+        assert list(new_lens)[:n] == [SENTINEL] * n
+        assert list(new_table)[:n * c["max_blocks"]] == [SENTINEL] * (n * c["max_blocks"])
+
+
+@settings(max_examples=300, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(calls())
+def test_failed_compaction_calls_change_nothing(c):
+    """The same contract for the compaction stage's own entry point."""
+    shape = kara.kara_shape(*c["shape"])
+    params = kara.kara_params(*c["params"])
+    n = len(c["lens"])
+    try:
+        pool = kara.Pool(c["n_blocks"], c["free"])
+    except kara.KaraError:
+        return
+    before = pool.snapshot()
+    new_table = _i32([SENTINEL] * (n * c["max_blocks"]))
+    new_lens = _i32([SENTINEL] * n)
+    st_ = kara.lib.kara_paged_compact(
+        ctypes.byref(shape), ctypes.byref(params), n, FAKE, c["n_blocks"], _i32(c["table"]), FAKE,
+        c["max_blocks"], _i32(c["lens"]), FAKE, FAKE, pool.handle, new_table, FAKE, new_lens, None)
+    if st_ == kara.KARA_OK:
+        assert n == 0
         return
     assert kara.kara_last_error()
     assert pool.snapshot() == before
