@@ -8,11 +8,15 @@
 //           one exp2 and one add per element, 16 independent elements per lane;
 //   kind 2  a streaming copy with 16-byte nontemporal loads and stores, eight
 //           loads in flight per lane;
-//   kind 3  kinds 0 and 1 interleaved in one wave exactly as the scoring kernel
-//           interleaves them: while the VALU turns one 64x32 logit tile into
-//           exponentials and sums, the matrix cores compute the next tile
-//           (2 * 128 MFMA flops per logit), in eight fenced regions of two
-//           MFMAs and four logits each;
+//   kind 3  the resident-key scoring kernel's tile loop without its per-tile
+//           work: eight waves per workgroup, 128 keys per wave held as the B
+//           operands of 16x16x32 bf16 MFMAs (2 * 128 flops per logit); per
+//           16-row tile, 32 fenced regions that each issue one of the next
+//           tile's first 24 MFMAs and one logit's multiply, exp2 and row-sum
+//           add per lane, then the last 8 MFMAs interleaved with the column
+//           FMAs (one per logit); query fragments read from LDS as the kernel
+//           reads them.  What it leaves out is the kernel's per-tile work: the
+//           row-sum reduction and exchange, the barrier and the query staging;
 //   kind 4  a streaming read with the copy's loads and launch shape; the loaded
 //           words are XOR-folded and stored only if they fold to a fixed
 //           value (in practice never), so nothing is written;
@@ -74,40 +78,86 @@ __global__ __launch_bounds__(kProbeThreads, 2) void probe_valu(float* dst, int64
   dst[(size_t)blockIdx.x * kProbeThreads + threadIdx.x] = (s[0] + s[1]) + (s[2] + s[3]);
 }
 
-__global__ __launch_bounds__(kProbeThreads, 2) void probe_mix(float* dst, int64_t iters, float c, float nb) {
-  const int lane = threadIdx.x & 63;
-  bf16x8 q0[8], q1[8], kf[8];
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+constexpr int kMixThreads = 512;       // eight waves, as the scoring kernel
+constexpr int kMixTiles = 8;           // 16-key N-tiles per wave
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__global__ __launch_bounds__(kMixThreads, 2) void probe_mix(float* dst, int64_t iters, float c) {
+  __shared__ __attribute__((aligned(16))) char qbuf[4][4096];     // four staged 16-row query tiles
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int grp = lane >> 4, kl = lane & 15;
+  for (int i = tid; i < 4 * 4096 / 16; i += kMixThreads) ((bf16x8*)&qbuf[0][0])[i] = operand(i, 7);
+  bf16x8 kf[kMixTiles][4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    q0[i] = operand(lane, i);
-    q1[i] = operand(lane, 8 + i);
-    kf[i] = operand(lane, 16 + i);
+  for (int nt = 0; nt < kMixTiles; ++nt)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) kf[nt][ks] = operand(lane + wave, 4 * nt + ks);
+  __syncthreads();
+  // the kernel's fragment address: row kl, 16-byte piece grp of a 32-dim quarter
+  const int qlane = kl * 64 + ((grp ^ ((kl >> 2) & 3)) << 4);
+  auto qfrag = [&](int t, int ks) { return *(const bf16x8*)&qbuf[t & 3][ks * 1024 + qlane]; };
+  f32x4 acc0[kMixTiles], acc1[kMixTiles];
+  float colacc[kMixTiles];
+#pragma unroll
+  for (int nt = 0; nt < kMixTiles; ++nt) {
+    acc0[nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    acc1[nt] = acc0[nt];
+    colacc[nt] = 0.0f;
   }
-  f32x16 a0 = {}, a1 = {}, b0 = {}, b1 = {};
-  float sp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  // MFMAs into (n0, n1) while the VALU consumes (v0, v1); the accumulators are
-  // carried across iterations so that no MFMA is loop-invariant.
-  auto half = [&](f32x16& n0, f32x16& n1, const f32x16& v0, const f32x16& v1) {
+  // one tile: exponentials and row sums of `cur` while the next tile's MFMAs
+  // accumulate into `nxt`; the column FMAs use weights that depend on the row
+  // sums (so that nothing is dead)
+  auto step = [&](f32x4 (&cur)[kMixTiles], f32x4 (&nxt)[kMixTiles], int t) {
+    bf16x8 qa[3];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      n0 = mfma(q0[i], kf[i], n0);
-      n1 = mfma(q1[i], kf[i], n1);
+    for (int ks = 0; ks < 3; ++ks) qa[ks] = qfrag(t + 1, ks);
+    float rp[4];
 #pragma unroll
-      for (int e = 4 * i; e < 4 * i + 4; ++e) {
-        const float x = e < 16 ? v0[e] : v1[e - 16];
-        sp[e & 3] += __builtin_amdgcn_exp2f(fmaf(x, c, nb));
+    for (int k = 0; k < 4 * kMixTiles; ++k) {
+      if (k < 3 * kMixTiles) {
+        const int ks = k / kMixTiles, nt = k % kMixTiles;
+        nxt[nt] = mfma16(qa[ks], kf[nt][ks], ks == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : nxt[nt]);
       }
+      const int nt = k / 4, r = k % 4;
+      const float x = __builtin_amdgcn_exp2f(cur[nt][r] * c);
+      cur[nt][r] = x;
+      rp[r] = nt == 0 ? x : rp[r] + x;
       __builtin_amdgcn_sched_barrier(0);
     }
+    const bf16x8 q3 = qfrag(t + 1, 3);
+#pragma unroll
+    for (int nt = 0; nt < kMixTiles / 2; ++nt) nxt[nt] = mfma16(q3, kf[nt][3], nxt[nt]);
+    __builtin_amdgcn_sched_barrier(0);
+    const float w0 = rp[0] * 1e-9f, w1 = rp[1] * 1e-9f, w2 = rp[2] * 1e-9f, w3 = rp[3] * 1e-9f;
+    auto cols = [&](int nt) {
+      float s = colacc[nt];
+      s = fmaf(cur[nt][0], w0, s);
+      s = fmaf(cur[nt][1], w1, s);
+      s = fmaf(cur[nt][2], w2, s);
+      s = fmaf(cur[nt][3], w3, s);
+      colacc[nt] = s;
+    };
+#pragma unroll
+    for (int nt = 0; nt < kMixTiles / 2; ++nt) {
+      nxt[kMixTiles / 2 + nt] = mfma16(q3, kf[kMixTiles / 2 + nt][3], nxt[kMixTiles / 2 + nt]);
+      cols(nt);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int nt = kMixTiles / 2; nt < kMixTiles; ++nt) cols(nt);
   };
   for (int64_t it = 0; it < iters; ++it) {
-    half(a0, a1, b0, b1);
-    half(b0, b1, a0, a1);
+    step(acc0, acc1, 2 * (int)(it & 1));
+    step(acc1, acc0, 2 * (int)(it & 1) + 1);
   }
-  float s = (sp[0] + sp[1]) + (sp[2] + sp[3]);
+  float s = 0.0f;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) s += 1e-30f * ((a0[r] + a1[r]) + (b0[r] + b1[r]));
-  dst[(size_t)blockIdx.x * kProbeThreads + threadIdx.x] = s;
+  for (int nt = 0; nt < kMixTiles; ++nt) s += colacc[nt] + 1e-30f * (acc0[nt][0] + acc1[nt][1]);
+  dst[(size_t)blockIdx.x * kMixThreads + tid] = s;
 }
 
 constexpr int kCopyUnroll = 8;
@@ -193,10 +243,13 @@ hipError_t launch_probe(int kind, int64_t iters, void* dst, const void* src, siz
       *work = (double)n * 16.0;                                       // bytes written
       break;
     }
-    case 3:
-      hipLaunchKernelGGL(probe_mix, dim3(grid), dim3(kProbeThreads), 0, stream, (float*)dst, iters, 1e-6f, -0.5f);
-      *work = waves * (double)iters * 2.0 * 2048.0;                   // logits (2 * 128 MFMA flops each)
+    case 3: {
+      // one eight-wave workgroup per CU (the same scratch: n_cu * 512 floats)
+      const unsigned g = (unsigned)n_cu;
+      hipLaunchKernelGGL(probe_mix, dim3(g), dim3(kMixThreads), 0, stream, (float*)dst, iters, 1e-6f);
+      *work = (double)g * (kMixThreads / 64) * (double)iters * 2.0 * 2048.0;   // logits (2 * 128 MFMA flops each)
       break;
+    }
     default:
       return hipErrorInvalidValue;
   }

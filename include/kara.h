@@ -481,10 +481,11 @@ kara_status kara_policy_sim(const kara_sim_config* config, kara_sim_result* resu
  *   KARA_PROBE_COPY  a streaming copy of n_bytes from src_d to dst_d with
  *                    16-byte nontemporal loads and stores; work in bytes read
  *                    plus bytes written.
- *   KARA_PROBE_MIX   MFMA and VALU work interleaved in one wave in the ratio
- *                    and order of the scoring kernel's inner loop (2 * 128
- *                    bf16 MFMA flops and one multiply-add, exp2 and add per
- *                    logit); work in logits.
+ *   KARA_PROBE_MIX   the resident-key scoring kernel's tile loop without its
+ *                    per-tile work: per logit 2 * 128 bf16 MFMA flops
+ *                    (16x16x32, keys resident) and a multiply, exp2, row-sum
+ *                    add and column FMA, interleaved as in that kernel, with
+ *                    the query fragments read from LDS; work in logits.
  *   KARA_PROBE_READ  a streaming read of n_bytes from src_d with the copy's
  *                    loads and launch shape; dst_d is a 4-byte sink (written
  *                    only if the loaded words fold to a fixed value, in
